@@ -1,0 +1,259 @@
+"""Benchmark: exact ring-emulated blockwise attention on one MI355X.
+
+Default workload (the headline): B=1, H=32, d=128, S=24000 over a P=4 ring
+(4 blocks of 6000 tokens), non-causal, bf16 Q/K/V ~ N(0,1)*0.5, fp32 out/lse.
+One step = one ra_ring_forward call that emulates every rank: 4 ring steps,
+each one attention launch over the 4 ranks' (Q block, K/V block) pairs with
+the sigma-rule merge fused into its epilogue.  Inputs are resident in HBM
+before timing starts.
+
+Prints ONE JSON line.  Extra objects:
+  roofline      -- the attention kernel: algorithmic flops per launch divided
+                   by its average launch time (HIP events on the launch stream
+                   during the timed region), against the bf16 dense MFMA peak.
+  merge         -- the standalone merge kernel at the GQA 1M-token share shape
+                   (4,194,304 row-heads x d128, 6.49 GB moved), in GB/s.
+  cpu_baseline  -- the fp64 CPU oracle on a bounded sample of the same
+                   workload (query rows x all keys), scaled to TFLOP/s.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 flop/clk (AMD's "2.5 PF" dense bf16)
+PEAK_F32_MFMA_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+# Measured rocprofv3 PMC traffic of the attention kernel (bytes per launch),
+# or None when not measured for the current kernel build.
+ATTN_TRAFFIC_BYTES = None
+
+
+def visible_pairs(w, rank=None):
+    """Visible (query, key) pairs of the emulated ranks."""
+    S, P = w.seq_q, w.P
+    if w.layout == "contig":
+        n = S // P
+        ranks = range(P) if (rank is None or rank < 0) else [rank]
+        return len(list(ranks)) * n * S
+    if w.layout == "kv_sharded":
+        return w.seq_q * w.seq_k
+    # causal layouts: query at position i sees i+1 keys
+    if w.layout == "zigzag_causal":
+        c = S // (2 * P)
+        if rank is None or rank < 0:
+            return S * (S + 1) // 2
+        return 2 * P * c * c + c
+    if w.layout == "contig_causal":
+        n = S // P
+        if rank is None or rank < 0:
+            return S * (S + 1) // 2
+        lo, hi = rank * n, (rank + 1) * n
+        return sum(i + 1 for i in range(lo, hi))
+    raise ValueError(w.layout)
+
+
+def flops_of(w, rank=None):
+    return 4.0 * w.head_dim * w.heads_q * w.batch * visible_pairs(w, rank)
+
+
+def cpu_baseline(w, q, k, v, budget_s=12.0):
+    """Time the oracle on a bounded sample of query rows against all keys."""
+    import numpy as np
+
+    from oracle import attention
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        threads = os.cpu_count()
+    kc, vc = k.cpu(), v.cpu()
+    causal = w.layout != "contig" and w.layout != "kv_sharded"
+    S = w.seq_q
+    rng = np.random.default_rng(0)
+    rows = 16
+    total_rows, total_t = 0, 0.0
+    while total_t < budget_s and total_rows < S:
+        sel = np.sort(rng.choice(S, size=min(rows, S), replace=False))
+        qs = q[:, sel].cpu()
+        t0 = time.perf_counter()
+        attention(qs, kc, vc, causal=causal, q_pos=sel)
+        dt = time.perf_counter() - t0
+        total_rows += len(sel)
+        total_t += dt
+        rows = min(rows * 2, 4096)
+        if dt > budget_s / 2:
+            break
+    # flops of the sampled rows: each sees all keys (non-causal) -> scale by
+    # the workload's mean keys per row otherwise
+    keys_per_row = visible_pairs(w) / (w.seq_q * 1.0) if causal else w.seq_k
+    fl = 4.0 * w.head_dim * w.heads_q * w.batch * total_rows * keys_per_row
+    return {
+        "value": fl / total_t / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{total_rows} query rows x {w.heads_q} heads x all {w.seq_k} keys "
+                  f"(of {w.seq_q} rows), fp64 numpy, {total_t:.1f} s",
+    }
+
+
+def merge_bench(steps=10):
+    """Standalone merge at the GQA 1M-token rank-share shape (>= 2 GB)."""
+    import torch
+
+    import ring_blockwise_softmax_amd as ra
+
+    B, S, H, D = 1, 131072, 32, 128
+    g = torch.Generator(device="cuda").manual_seed(44)
+    out = torch.randn(B, S, H, D, device="cuda", generator=g)
+    bout = torch.randn(B, S, H, D, device="cuda", generator=g)
+    lse = torch.randn(B, H, S, device="cuda", generator=g)
+    blse = torch.randn(B, H, S, device="cuda", generator=g)
+    for _ in range(3):
+        ra.merge(out, lse, bout, blse)
+    torch.cuda.synchronize()
+    ra.profile_enable(True)
+    for _ in range(steps):
+        ra.merge(out, lse, bout, blse)
+    prof = ra.profile_read()
+    ra.profile_enable(False)
+    n, ms = prof["merge"]
+    per = ms / n
+    nbytes = B * S * H * (3 * 4 * D + 12)
+    # plain device copy of the same byte count for reference
+    src = torch.empty(nbytes // 2, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_ms = e0.elapsed_time(e1) / steps
+    del out, bout, lse, blse, src, dst
+    torch.cuda.empty_cache()
+    return {
+        "shape": f"B{B} S{S} H{H} d{D} fp32",
+        "bytes": nbytes,
+        "ms": per,
+        "achieved_GBs": nbytes / per / 1e6,
+        "peak_GBs": PEAK_HBM_GBS,
+        "frac": nbytes / per / 1e6 / PEAK_HBM_GBS,
+        "copy_GBs": nbytes / copy_ms / 1e6,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="mha24k")
+    ap.add_argument("--order", default="ring", choices=["ring", "tokenring"])
+    ap.add_argument("--unfused", action="store_true", help="separate merge kernel")
+    ap.add_argument("--rank", type=int, default=None, help="emulate one rank's share only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-merge", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the ring is emulated in one device's memory; "
+              "--gpus above 1 is not supported by this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import ring_blockwise_softmax_amd as ra
+    from ring_blockwise_softmax_amd.workloads import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    rank = w.rank if args.rank is None else args.rank
+    q, k, v = make_inputs(w, device="cuda")
+    runner = ra.RingRunner(q, k, v, w.P, layout=w.layout, order=args.order, rank=rank,
+                           fuse_merge=not args.unfused)
+    for _ in range(args.warmup):
+        runner.run()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ra.profile_enable(True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        runner.run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    prof = ra.profile_read()
+    ra.profile_enable(False)
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    total_flops = flops_of(w, rank)
+    tflops = total_flops / (ms_step / 1e3) / 1e12
+    n_attn, attn_ms = prof["attn"]
+    launches_per_step = n_attn / args.steps
+    attn_avg_ms = attn_ms / n_attn
+    flops_per_launch = total_flops / launches_per_step
+    achieved = flops_per_launch / (attn_avg_ms / 1e3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
+
+    rec = {
+        "metric": "attention TFLOP/s + % bf16 MFMA peak at S=24000, H=32, d=128, 1 GPU",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1)*%g Q/K/V)" % w.std,
+        "config": {
+            "workload": f"{w.name}: B{w.batch} Hq{w.heads_q}/Hkv{w.heads_kv} d{w.head_dim} "
+                        f"S{w.seq_q} over P={w.P} ({w.layout}), {'all ranks' if rank < 0 else f'rank {rank}'}",
+            "global_batch": w.batch,
+            "seq_len": w.seq_q,
+            "P": w.P,
+            "layout": w.layout,
+            "order": args.order,
+            "fuse_merge": not args.unfused,
+            "flops_per_step": total_flops,
+            "parallelism": "single GPU, ring emulated in device memory",
+        },
+        "pct_peak": round(100.0 * tflops / peak, 2),
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "attn_fwd_bf16<128> (fused merge epilogue)" if w.dtype == "bf16" else "attn_fwd_f32",
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": ATTN_TRAFFIC_BYTES,
+            "launches_per_step": launches_per_step,
+            "avg_launch_ms": round(attn_avg_ms, 4),
+            "flops_per_launch": flops_per_launch,
+        },
+    }
+    if not args.no_merge:
+        rec["merge"] = merge_bench()
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, q, k, v)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

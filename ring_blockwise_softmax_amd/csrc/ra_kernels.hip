@@ -1,0 +1,772 @@
+// HIP kernels for exact blockwise attention on gfx950 (MI355X).
+//
+// What is computed (TokenRing review, pith.science, "What carries the
+// argument"; Ring Attention record, anthology-of-the-sota): attention of a
+// block of query rows against one or two key/value segments, returning the
+// normalised partial output and its natural-log row log-sum-exp, optionally
+// folded straight into a running (out, lse) pair with the sigma rule
+//     out <- out - sigmoid(blse - lse) * (out - bout)
+//     lse <- lse - ln sigmoid(lse - blse)
+// evaluated in its overflow-free form max(lse, blse) + log1p(exp(-|diff|)).
+//
+// Kernel shape (bf16 path, one work-group = 4 waves = 128 packed query rows):
+//  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
+//    the key index runs down the MFMA M dimension and the query index across
+//    N, so each lane owns one query column and the softmax row reductions are
+//    register-local plus one v_permlane32_swap between the lane halves.
+//  * The P*V product is likewise out^T = V^T P^T: the exponentiated score
+//    registers are already laid out as the B operand, so P never touches LDS.
+//    The V^T A operand comes from the row-major V tile through
+//    ds_read_b64_tr_b16 (16-lane transpose reads), so V is staged as loaded.
+//  * K/V tiles of 64 keys are double-buffered in LDS; the next tile's global
+//    loads are in flight while the current one is consumed (one barrier/tile).
+//  * Online softmax in the exp2 domain with a lazy rescale: the running
+//    maximum used for exponentiation only moves when a row's maximum grows
+//    by more than 2^8, so the accumulator is rarely rescaled; the final
+//    normalisation uses the same reference, so the result is unchanged.
+//  * Work tiles are assigned XCD-contiguously: consecutive tiles of one
+//    (batch, head) land on the same XCD and share its L2 copy of K/V.
+//
+// The fp32 path has the same structure on v_mfma_f32_32x32x2_f32, with no
+// rounding of inputs or probabilities anywhere.
+
+#include <hip/hip_runtime.h>
+
+#include "ra_internal.h"
+
+namespace ra {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr int kThreads = 256;
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kRescaleThreshold = 8.0f;  // log2 units
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+
+// max / sum of a value with its partner lane in the other half of the wave.
+__device__ __forceinline__ float max_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return __int_as_float(r[0]) + __int_as_float(r[1]);
+}
+
+// ---------------------------------------------------------------------------
+// Work decoding shared by both attention kernels.
+// ---------------------------------------------------------------------------
+struct Tile {
+  int b, hb, item, qt, split;
+};
+
+__device__ __forceinline__ bool decode_tile(const AttnArgs &a, Tile &t) {
+  const int L = blockIdx.x;
+  const int idx = (L & 7) * a.per_xcd + (L >> 3);
+  if (idx >= a.n_work) return false;
+  const int tt = idx % a.ntiles;
+  const int rest = idx / a.ntiles;
+  t.hb = rest % a.nhb;
+  t.b = rest / a.nhb;
+  int it = 0;
+  while (it + 1 < a.nitems && tt >= a.items[it + 1].tile0) ++it;
+  t.item = it;
+  const int e = tt - a.items[it].tile0;
+  t.qt = e / a.items[it].nsplit;
+  t.split = e % a.items[it].nsplit;
+  return true;
+}
+
+// Key range [lo, hi) of segment s for this tile (split and causal limits).
+struct SegRange {
+  int kv_start, kpos0, causal, lo, hi;
+};
+
+__device__ __forceinline__ SegRange seg_range(const KItem &it, int s, int split, int qpos_max) {
+  SegRange r;
+  r.kv_start = it.seg[s].kv_start;
+  r.kpos0 = it.seg[s].kpos0;
+  r.causal = it.seg[s].causal;
+  r.lo = 0;
+  r.hi = it.seg[s].kv_len;
+  if (it.nsplit > 1) {
+    r.lo = split * it.split_len;
+    r.hi = min(r.hi, r.lo + it.split_len);
+  }
+  if (r.causal) r.hi = min(r.hi, qpos_max - r.kpos0 + 1);
+  if (r.hi < r.lo) r.hi = r.lo;
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// Epilogue: normalise, then write, merge or store a split partial.
+// acc holds out^T for this lane's query column: element r of block mb is
+// d = 32*mb + 8*(r/4) + 4*g + (r%4).
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ void epilogue(const AttnArgs &a, const KItem &it, const Tile &t, int prow,
+                                         bool row_ok, f32x16 (&acc)[D / 32], float m_run,
+                                         float l_part, int g) {
+  const float l_tot = sum_halves(l_part);
+  if (!row_ok) return;
+  const int tok = prow / a.GP;
+  const int h = t.hb * a.GP + prow % a.GP;
+  const bool empty = !(l_tot > 0.0f);
+  const float inv = empty ? 0.0f : 1.0f / l_tot;
+  const float blse = empty ? neg_inf() : (m_run + __log2f(l_tot)) * kLn2;
+
+  if (a.mode == kSplit) {
+    const int64_t prow_idx = ((int64_t)(t.split * a.B + t.b) * a.Hq + h) * a.part_rows + tok;
+    float *po = a.part_out + prow_idx * D;
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d0 = 32 * mb + 8 * i4 + 4 * g;
+        f32x4 v = {acc[mb][4 * i4] * inv, acc[mb][4 * i4 + 1] * inv, acc[mb][4 * i4 + 2] * inv,
+                   acc[mb][4 * i4 + 3] * inv};
+        *(f32x4 *)(po + d0) = v;
+      }
+    if (g == 0) a.part_lse[prow_idx] = blse;
+    return;
+  }
+
+  const int orow = it.o_row0 + tok;
+  float *op = a.out + (int64_t)t.b * a.o_sb + (int64_t)orow * a.o_ss + (int64_t)h * a.o_sh;
+  float *lp = a.lse + (int64_t)t.b * a.l_sb + (int64_t)orow * a.l_ss + (int64_t)h * a.l_sh;
+
+  if (a.mode == kMerge && !it.first) {
+    const float lse_run = *lp;
+    if (empty) return;  // an empty partial is the identity
+    if (lse_run == neg_inf()) {
+#pragma unroll
+      for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int d0 = 32 * mb + 8 * i4 + 4 * g;
+          f32x4 v = {acc[mb][4 * i4] * inv, acc[mb][4 * i4 + 1] * inv, acc[mb][4 * i4 + 2] * inv,
+                     acc[mb][4 * i4 + 3] * inv};
+          *(f32x4 *)(op + d0) = v;
+        }
+      if (g == 0) *lp = blse;
+      return;
+    }
+    const float diff = blse - lse_run;
+    const float w = 1.0f / (1.0f + __expf(-diff));
+    const float new_lse = fmaxf(lse_run, blse) + log1pf(__expf(-fabsf(diff)));
+#pragma unroll
+    for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d0 = 32 * mb + 8 * i4 + 4 * g;
+        f32x4 o = *(const f32x4 *)(op + d0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = o[j] - w * (o[j] - acc[mb][4 * i4 + j] * inv);
+        *(f32x4 *)(op + d0) = o;
+      }
+    if (g == 0) *lp = new_lse;
+    return;
+  }
+
+#pragma unroll
+  for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int d0 = 32 * mb + 8 * i4 + 4 * g;
+      f32x4 v = {acc[mb][4 * i4] * inv, acc[mb][4 * i4 + 1] * inv, acc[mb][4 * i4 + 2] * inv,
+                 acc[mb][4 * i4 + 3] * inv};
+      *(f32x4 *)(op + d0) = v;
+    }
+  if (g == 0) *lp = blse;
+}
+
+// ---------------------------------------------------------------------------
+// bf16 kernel
+// ---------------------------------------------------------------------------
+template <int D>
+struct Bf16Cfg {
+  static constexpr int KT = kKTileBF16;          // keys per LDS tile
+  static constexpr int QT = kQTileBF16;          // packed rows per work-group
+  static constexpr int LD = D + 8;               // LDS row pitch (elements)
+  static constexpr int CHUNKS = KT * D / 8;      // 16-byte chunks per K (or V) tile
+  static constexpr int CPT = CHUNKS / kThreads;  // chunks per thread
+  static constexpr int TILE_ELEMS = KT * LD;
+  static constexpr size_t LDS_BYTES = 2 /*K,V*/ * 2 /*buffers*/ * TILE_ELEMS * sizeof(bf16);
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(const AttnArgs a) {
+  using C = Bf16Cfg<D>;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  bf16 *smem = reinterpret_cast<bf16 *>(smem_raw);
+
+  Tile t;
+  if (!decode_tile(a, t)) return;
+  const KItem &it = a.items[t.item];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int n = lane & 31;  // query column of this lane
+  const int g = lane >> 5;  // lane half
+  const int i16 = lane & 15, G16 = lane >> 4;
+
+  const int rows_total = it.q_len * a.GP;
+  const int tile_row0 = t.qt * C::QT;
+  const int wave_row0 = tile_row0 + wave * 32;
+  const int prow = wave_row0 + n;
+  const bool row_ok = prow < rows_total;
+  const int hkv = (t.hb * a.GP) / a.G;
+
+  // Positions of this lane's query, of the wave's rows and of the tile's rows.
+  const int qpos = it.qpos0 + (row_ok ? prow : rows_total - 1) / a.GP;
+  const int wave_last = min(wave_row0 + 31, rows_total - 1);
+  const int wave_qpos_min = it.qpos0 + min(wave_row0, rows_total - 1) / a.GP;
+  const int wave_qpos_max = it.qpos0 + wave_last / a.GP;
+  const bool wave_active = wave_row0 < rows_total;
+  const int tile_qpos_max = it.qpos0 + (min(tile_row0 + C::QT, rows_total) - 1) / a.GP;
+
+  // Q fragment (B operand of S^T = K Q^T): d = 16*kc + 8*g + 0..7.
+  bf16x8 qf[D / 16];
+  {
+    const int tok = (row_ok ? prow : 0) / a.GP;
+    const int h = t.hb * a.GP + (row_ok ? prow : 0) % a.GP;
+    const bf16 *qp = reinterpret_cast<const bf16 *>(a.q) + (int64_t)t.b * a.q_sb +
+                     (int64_t)(it.q_start + tok) * a.q_ss + (int64_t)h * a.q_sh + 8 * g;
+#pragma unroll
+    for (int kc = 0; kc < D / 16; ++kc) {
+      if (row_ok)
+        qf[kc] = *(const bf16x8 *)(qp + 16 * kc);
+      else
+        qf[kc] = bf16x8{};
+    }
+  }
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int mb = 0; mb < D / 32; ++mb) acc[mb] = f32x16{};
+  float m_run = neg_inf();
+  float l_part = 0.0f;
+
+  // Key tiles of the (up to two) segments, flattened.
+  SegRange sr0 = seg_range(it, 0, t.split, tile_qpos_max);
+  SegRange sr1 = sr0;
+  int nt0 = (sr0.hi - sr0.lo + C::KT - 1) / C::KT;
+  int nt1 = 0;
+  if (it.nseg > 1) {
+    sr1 = seg_range(it, 1, t.split, tile_qpos_max);
+    nt1 = (sr1.hi - sr1.lo + C::KT - 1) / C::KT;
+  }
+  const int ntiles = nt0 + nt1;
+
+  const bf16 *kbase = reinterpret_cast<const bf16 *>(a.k) + (int64_t)t.b * a.k_sb + (int64_t)hkv * a.k_sh;
+  const bf16 *vbase = reinterpret_cast<const bf16 *>(a.v) + (int64_t)t.b * a.v_sb + (int64_t)hkv * a.v_sh;
+
+  bf16x8 kreg[C::CPT], vreg[C::CPT];
+
+  auto tile_info = [&](int ti, SegRange &sr, int &key0) {
+    if (ti < nt0) {
+      sr = sr0;
+      key0 = sr0.lo + ti * C::KT;
+    } else {
+      sr = sr1;
+      key0 = sr1.lo + (ti - nt0) * C::KT;
+    }
+  };
+
+  auto gload = [&](int ti) {
+    SegRange sr;
+    int key0;
+    tile_info(ti, sr, key0);
+    const int nvalid = sr.hi - key0;
+#pragma unroll
+    for (int u = 0; u < C::CPT; ++u) {
+      const int c = tid + kThreads * u;
+      const int key = c / (D / 8);
+      const int col = (c % (D / 8)) * 8;
+      if (key < nvalid) {
+        const int64_t row = sr.kv_start + key0 + key;
+        kreg[u] = *(const bf16x8 *)(kbase + row * a.k_ss + col);
+        vreg[u] = *(const bf16x8 *)(vbase + row * a.v_ss + col);
+      } else {
+        kreg[u] = bf16x8{};
+        vreg[u] = bf16x8{};
+      }
+    }
+  };
+
+  auto lstore = [&](int buf) {
+    bf16 *Ks = smem + buf * 2 * C::TILE_ELEMS;
+    bf16 *Vs = Ks + C::TILE_ELEMS;
+#pragma unroll
+    for (int u = 0; u < C::CPT; ++u) {
+      const int c = tid + kThreads * u;
+      const int key = c / (D / 8);
+      const int col = (c % (D / 8)) * 8;
+      *(bf16x8 *)(Ks + key * C::LD + col) = kreg[u];
+      *(bf16x8 *)(Vs + key * C::LD + col) = vreg[u];
+    }
+  };
+
+  if (ntiles > 0) {
+    gload(0);
+    lstore(0);
+  }
+  __syncthreads();
+
+  for (int ti = 0; ti < ntiles; ++ti) {
+    const int buf = ti & 1;
+    if (ti + 1 < ntiles) gload(ti + 1);
+
+    SegRange sr;
+    int key0;
+    tile_info(ti, sr, key0);
+    const bf16 *Ks = smem + buf * 2 * C::TILE_ELEMS;
+    const bf16 *Vs = Ks + C::TILE_ELEMS;
+
+#pragma unroll
+    for (int sub = 0; sub < C::KT / 32; ++sub) {
+      const int kb = key0 + sub * 32;  // first key of this sub-tile (segment-local)
+      // Wave-uniform skip: no rows, no valid keys, or every key after every row.
+      const bool skip = !wave_active || kb >= sr.hi ||
+                        (sr.causal && sr.kpos0 + kb > wave_qpos_max);
+      if (skip) continue;
+      const bool need_mask = (kb + 32 > sr.hi) || (sr.causal && sr.kpos0 + kb + 31 > wave_qpos_min);
+
+      // S^T = K Q^T for 32 keys x 32 queries.
+      f32x16 s = f32x16{};
+#pragma unroll
+      for (int kc = 0; kc < D / 16; ++kc) {
+        const bf16x8 ka = *(const bf16x8 *)(Ks + (sub * 32 + n) * C::LD + 16 * kc + 8 * g);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kc], s, 0, 0, 0);
+      }
+
+      if (need_mask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kb + 8 * (r >> 2) + 4 * g + (r & 3);
+          const bool vis = key < sr.hi && (!sr.causal || sr.kpos0 + key <= qpos);
+          if (!vis) s[r] = neg_inf();
+        }
+      }
+
+      // Row maximum (log2 domain) and lazy rescale.
+      float mx = s[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+      mx = max_halves(mx) * a.scale_log2;
+      const float m_new = fmaxf(m_run, mx);
+      const bool need = m_new > m_run + kRescaleThreshold;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+        m_run = need ? m_new : m_run;
+        l_part *= alpha;
+#pragma unroll
+        for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[mb][r] *= alpha;
+      }
+      const float moff = (m_run == neg_inf()) ? 0.0f : m_run;
+
+      // P = exp2(s * scale_log2 - m).  The row sum takes the fp32 values
+      // (so lse is exact to fp32); the P*V product takes them rounded to
+      // bf16 (round to nearest even).
+      bf16x8 pb[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * c + e], a.scale_log2, -moff));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * c + e + 1], a.scale_log2, -moff));
+          const bf16x2 pp = {(bf16)p0, (bf16)p1};
+          pb[c][e] = pp[0];
+          pb[c][e + 1] = pp[1];
+          l_part += p0 + p1;
+        }
+      }
+
+      // out^T += V^T P^T over two 16-key chunks.
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int krow = sub * 32 + 16 * c + 4 * g + (i16 >> 2);
+#pragma unroll
+        for (int mb = 0; mb < D / 32; ++mb) {
+          const int dcol = 32 * mb + 16 * (G16 & 1) + 4 * (i16 & 3);
+          const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4 *)(Vs + krow * C::LD + dcol));
+          const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4 *)(Vs + (krow + 8) * C::LD + dcol));
+          const s16x8 vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pb[c],
+                                                            acc[mb], 0, 0, 0);
+        }
+      }
+    }
+
+    if (ti + 1 < ntiles) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  epilogue<D>(a, it, t, prow, row_ok, acc, m_run, l_part, g);
+}
+
+// ---------------------------------------------------------------------------
+// fp32 kernel (exact path): v_mfma_f32_32x32x2_f32, no rounding.
+// ---------------------------------------------------------------------------
+template <int D>
+struct F32Cfg {
+  static constexpr int KT = kKTileF32;
+  static constexpr int QT = kQTileF32;
+  static constexpr int LD = D + 4;
+  static constexpr int CHUNKS = KT * D / 4;
+  static constexpr int CPT = CHUNKS / kThreads;
+  static constexpr int TILE_ELEMS = KT * LD;
+  static constexpr size_t LDS_BYTES = 2 * 2 * TILE_ELEMS * sizeof(float);
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void attn_fwd_f32(const AttnArgs a) {
+  using C = F32Cfg<D>;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  float *smem = reinterpret_cast<float *>(smem_raw);
+
+  Tile t;
+  if (!decode_tile(a, t)) return;
+  const KItem &it = a.items[t.item];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int n = lane & 31;
+  const int g = lane >> 5;
+
+  const int rows_total = it.q_len * a.GP;
+  const int tile_row0 = t.qt * C::QT;
+  const int wave_row0 = tile_row0 + wave * 32;
+  const int prow = wave_row0 + n;
+  const bool row_ok = prow < rows_total;
+  const int hkv = (t.hb * a.GP) / a.G;
+  const int qpos = it.qpos0 + (row_ok ? prow : rows_total - 1) / a.GP;
+  const int wave_last = min(wave_row0 + 31, rows_total - 1);
+  const int wave_qpos_min = it.qpos0 + min(wave_row0, rows_total - 1) / a.GP;
+  const int wave_qpos_max = it.qpos0 + wave_last / a.GP;
+  const bool wave_active = wave_row0 < rows_total;
+  const int tile_qpos_max = it.qpos0 + (min(tile_row0 + C::QT, rows_total) - 1) / a.GP;
+
+  // Q fragment: lane half g holds d = (D/2)*g + kc, kc = 0 .. D/2-1.
+  float qf[D / 2];
+  {
+    const int tok = (row_ok ? prow : 0) / a.GP;
+    const int h = t.hb * a.GP + (row_ok ? prow : 0) % a.GP;
+    const float *qp = reinterpret_cast<const float *>(a.q) + (int64_t)t.b * a.q_sb +
+                      (int64_t)(it.q_start + tok) * a.q_ss + (int64_t)h * a.q_sh + (D / 2) * g;
+#pragma unroll
+    for (int j = 0; j < D / 8; ++j) {
+      f32x4 v = row_ok ? *(const f32x4 *)(qp + 4 * j) : f32x4{};
+      qf[4 * j] = v[0];
+      qf[4 * j + 1] = v[1];
+      qf[4 * j + 2] = v[2];
+      qf[4 * j + 3] = v[3];
+    }
+  }
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int mb = 0; mb < D / 32; ++mb) acc[mb] = f32x16{};
+  float m_run = neg_inf();
+  float l_part = 0.0f;
+
+  SegRange sr0 = seg_range(it, 0, t.split, tile_qpos_max);
+  SegRange sr1 = sr0;
+  int nt0 = (sr0.hi - sr0.lo + C::KT - 1) / C::KT;
+  int nt1 = 0;
+  if (it.nseg > 1) {
+    sr1 = seg_range(it, 1, t.split, tile_qpos_max);
+    nt1 = (sr1.hi - sr1.lo + C::KT - 1) / C::KT;
+  }
+  const int ntiles = nt0 + nt1;
+
+  const float *kbase = reinterpret_cast<const float *>(a.k) + (int64_t)t.b * a.k_sb + (int64_t)hkv * a.k_sh;
+  const float *vbase = reinterpret_cast<const float *>(a.v) + (int64_t)t.b * a.v_sb + (int64_t)hkv * a.v_sh;
+
+  f32x4 kreg[C::CPT], vreg[C::CPT];
+
+  auto tile_info = [&](int ti, SegRange &sr, int &key0) {
+    if (ti < nt0) {
+      sr = sr0;
+      key0 = sr0.lo + ti * C::KT;
+    } else {
+      sr = sr1;
+      key0 = sr1.lo + (ti - nt0) * C::KT;
+    }
+  };
+  auto gload = [&](int ti) {
+    SegRange sr;
+    int key0;
+    tile_info(ti, sr, key0);
+    const int nvalid = sr.hi - key0;
+#pragma unroll
+    for (int u = 0; u < C::CPT; ++u) {
+      const int c = tid + kThreads * u;
+      const int key = c / (D / 4);
+      const int col = (c % (D / 4)) * 4;
+      if (key < nvalid) {
+        const int64_t row = sr.kv_start + key0 + key;
+        kreg[u] = *(const f32x4 *)(kbase + row * a.k_ss + col);
+        vreg[u] = *(const f32x4 *)(vbase + row * a.v_ss + col);
+      } else {
+        kreg[u] = f32x4{};
+        vreg[u] = f32x4{};
+      }
+    }
+  };
+  auto lstore = [&](int buf) {
+    float *Ks = smem + buf * 2 * C::TILE_ELEMS;
+    float *Vs = Ks + C::TILE_ELEMS;
+#pragma unroll
+    for (int u = 0; u < C::CPT; ++u) {
+      const int c = tid + kThreads * u;
+      const int key = c / (D / 4);
+      const int col = (c % (D / 4)) * 4;
+      *(f32x4 *)(Ks + key * C::LD + col) = kreg[u];
+      *(f32x4 *)(Vs + key * C::LD + col) = vreg[u];
+    }
+  };
+
+  if (ntiles > 0) {
+    gload(0);
+    lstore(0);
+  }
+  __syncthreads();
+
+  for (int ti = 0; ti < ntiles; ++ti) {
+    const int buf = ti & 1;
+    if (ti + 1 < ntiles) gload(ti + 1);
+    SegRange sr;
+    int kb;
+    tile_info(ti, sr, kb);
+    const float *Ks = smem + buf * 2 * C::TILE_ELEMS;
+    const float *Vs = Ks + C::TILE_ELEMS;
+
+    const bool skip = !wave_active || kb >= sr.hi || (sr.causal && sr.kpos0 + kb > wave_qpos_max);
+    if (!skip) {
+      const bool need_mask = (kb + 32 > sr.hi) || (sr.causal && sr.kpos0 + kb + 31 > wave_qpos_min);
+      f32x16 s = f32x16{};
+#pragma unroll
+      for (int j = 0; j < D / 8; ++j) {
+        const f32x4 ka = *(const f32x4 *)(Ks + n * C::LD + (D / 2) * g + 4 * j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          s = __builtin_amdgcn_mfma_f32_32x32x2f32(ka[e], qf[4 * j + e], s, 0, 0, 0);
+      }
+      if (need_mask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kb + 8 * (r >> 2) + 4 * g + (r & 3);
+          const bool vis = key < sr.hi && (!sr.causal || sr.kpos0 + key <= qpos);
+          if (!vis) s[r] = neg_inf();
+        }
+      }
+      float mx = s[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+      mx = max_halves(mx) * a.scale_log2;
+      const float m_new = fmaxf(m_run, mx);
+      const bool need = m_new > m_run + kRescaleThreshold;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+        m_run = need ? m_new : m_run;
+        l_part *= alpha;
+#pragma unroll
+        for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[mb][r] *= alpha;
+      }
+      const float moff = (m_run == neg_inf()) ? 0.0f : m_run;
+      float p[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], a.scale_log2, -moff));
+        l_part += p[r];
+      }
+      // out^T += V^T P^T: register r of P pairs key 8*(r/4) + 4*g + r%4.
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int krow = 8 * (r >> 2) + 4 * g + (r & 3);
+#pragma unroll
+        for (int mb = 0; mb < D / 32; ++mb)
+          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x2f32(Vs[krow * C::LD + 32 * mb + n], p[r], acc[mb], 0, 0, 0);
+      }
+    }
+
+    if (ti + 1 < ntiles) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  epilogue<D>(a, it, t, prow, row_ok, acc, m_run, l_part, g);
+}
+
+// ---------------------------------------------------------------------------
+// Standalone merge: one float4 of one (row, head) per thread.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
+  const int per_row = a.D / 4;
+  const int64_t f = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = (int64_t)a.B * a.total_rows * a.H * per_row;
+  if (f >= total) return;
+  const int d4 = (int)(f % per_row);
+  int64_t rest = f / per_row;
+  const int h = (int)(rest % a.H);
+  rest /= a.H;
+  const int row = (int)(rest % a.total_rows);
+  const int b = (int)(rest / a.total_rows);
+  int k = 0;
+  while (k + 1 < a.nranges && row >= a.ranges[k + 1].prefix) ++k;
+  const int off = row - a.ranges[k].prefix;
+  const int dr = a.ranges[k].dst0 + off;
+  const int sr = a.ranges[k].src0 + off;
+
+  float *op = a.out + (int64_t)b * a.o_sb + (int64_t)dr * a.o_ss + (int64_t)h * a.o_sh + 4 * d4;
+  float *lp = a.lse + (int64_t)b * a.l_sb + (int64_t)dr * a.l_ss + (int64_t)h * a.l_sh;
+  const float *bop = a.bout + (int64_t)b * a.bo_sb + (int64_t)sr * a.bo_ss + (int64_t)h * a.bo_sh + 4 * d4;
+  const float *blp = a.blse + (int64_t)b * a.bl_sb + (int64_t)sr * a.bl_ss + (int64_t)h * a.bl_sh;
+
+  const float blse = *blp;
+  if (blse == neg_inf()) return;  // identity
+  const float lse = *lp;
+  const f32x4 bo = __builtin_nontemporal_load((const f32x4 *)bop);
+  if (lse == neg_inf()) {
+    *(f32x4 *)op = bo;
+    if (d4 == 0) *lp = blse;
+    return;
+  }
+  const float diff = blse - lse;
+  const float w = 1.0f / (1.0f + __expf(-diff));
+  f32x4 o = *(const f32x4 *)op;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) o[j] = o[j] - w * (o[j] - bo[j]);
+  *(f32x4 *)op = o;
+  if (d4 == 0) *lp = fmaxf(lse, blse) + log1pf(__expf(-fabsf(diff)));
+}
+
+// ---------------------------------------------------------------------------
+// Split-K reduction: fold the partials of each row in split order, then
+// write or merge the result.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void split_reduce_kernel(const SplitArgs a) {
+  const int per_row = a.D / 4;
+  const int64_t f = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = (int64_t)a.B * a.H * a.rows * per_row;
+  if (f >= total) return;
+  const int d4 = (int)(f % per_row);
+  int64_t rest = f / per_row;
+  const int tok = (int)(rest % a.rows);
+  rest /= a.rows;
+  const int h = (int)(rest % a.H);
+  const int b = (int)(rest / a.H);
+
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  float l = neg_inf();
+  for (int s = 0; s < a.nsplit; ++s) {
+    const int64_t pr = ((int64_t)(s * a.B + b) * a.H + h) * a.rows + tok;
+    const float bl = a.part_lse[pr];
+    if (bl == neg_inf()) continue;
+    const f32x4 bo = *(const f32x4 *)(a.part_out + pr * a.D + 4 * d4);
+    if (l == neg_inf()) {
+      o = bo;
+      l = bl;
+      continue;
+    }
+    const float diff = bl - l;
+    const float w = 1.0f / (1.0f + __expf(-diff));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = o[j] - w * (o[j] - bo[j]);
+    l = fmaxf(l, bl) + log1pf(__expf(-fabsf(diff)));
+  }
+
+  const int orow = a.o_row0 + tok;
+  float *op = a.out + (int64_t)b * a.o_sb + (int64_t)orow * a.o_ss + (int64_t)h * a.o_sh + 4 * d4;
+  float *lp = a.lse + (int64_t)b * a.l_sb + (int64_t)orow * a.l_ss + (int64_t)h * a.l_sh;
+  if (a.mode == kMerge && !a.first) {
+    if (l == neg_inf()) return;
+    const float lr = *lp;
+    if (lr != neg_inf()) {
+      const float diff = l - lr;
+      const float w = 1.0f / (1.0f + __expf(-diff));
+      f32x4 r = *(const f32x4 *)op;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) r[j] = r[j] - w * (r[j] - o[j]);
+      o = r;
+      l = fmaxf(lr, l) + log1pf(__expf(-fabsf(diff)));
+    }
+  }
+  *(f32x4 *)op = o;
+  if (d4 == 0) *lp = l;
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+template <typename K>
+static int set_lds(K kernel, size_t bytes, bool &done) {
+  if (!done) {
+    hipError_t e = hipFuncSetAttribute((const void *)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e != hipSuccess) return (int)e;
+    done = true;
+  }
+  return 0;
+}
+
+int launch_attn(const AttnArgs &a, int dtype, int head_dim, void *stream) {
+  const dim3 grid(a.per_xcd * 8), block(kThreads);
+  hipStream_t s = (hipStream_t)stream;
+  int rc = 0;
+  if (dtype == 0) {
+    if (head_dim == 128) {
+      static bool done = false;
+      if ((rc = set_lds(attn_fwd_bf16<128>, Bf16Cfg<128>::LDS_BYTES, done))) return rc;
+      hipLaunchKernelGGL(attn_fwd_bf16<128>, grid, block, Bf16Cfg<128>::LDS_BYTES, s, a);
+    } else {
+      static bool done = false;
+      if ((rc = set_lds(attn_fwd_bf16<64>, Bf16Cfg<64>::LDS_BYTES, done))) return rc;
+      hipLaunchKernelGGL(attn_fwd_bf16<64>, grid, block, Bf16Cfg<64>::LDS_BYTES, s, a);
+    }
+  } else {
+    if (head_dim == 128) {
+      static bool done = false;
+      if ((rc = set_lds(attn_fwd_f32<128>, F32Cfg<128>::LDS_BYTES, done))) return rc;
+      hipLaunchKernelGGL(attn_fwd_f32<128>, grid, block, F32Cfg<128>::LDS_BYTES, s, a);
+    } else {
+      static bool done = false;
+      if ((rc = set_lds(attn_fwd_f32<64>, F32Cfg<64>::LDS_BYTES, done))) return rc;
+      hipLaunchKernelGGL(attn_fwd_f32<64>, grid, block, F32Cfg<64>::LDS_BYTES, s, a);
+    }
+  }
+  return (int)hipGetLastError();
+}
+
+int launch_merge(const MergeArgs &a, void *stream) {
+  const int64_t total = (int64_t)a.B * a.total_rows * a.H * (a.D / 4);
+  if (total == 0) return 0;
+  const dim3 grid((unsigned)((total + 255) / 256)), block(256);
+  hipLaunchKernelGGL(merge_kernel, grid, block, 0, (hipStream_t)stream, a);
+  return (int)hipGetLastError();
+}
+
+int launch_split_reduce(const SplitArgs &a, void *stream) {
+  const int64_t total = (int64_t)a.B * a.H * a.rows * (a.D / 4);
+  if (total == 0) return 0;
+  const dim3 grid((unsigned)((total + 255) / 256)), block(256);
+  hipLaunchKernelGGL(split_reduce_kernel, grid, block, 0, (hipStream_t)stream, a);
+  return (int)hipGetLastError();
+}
+
+}  // namespace ra
