@@ -1,0 +1,150 @@
+"""Argument checks of the C ABI, on a machine with no GPU.
+
+Validation is pure host code that runs before any HIP call, so every bad
+argument below is reported with its status code here, and nothing is
+enqueued.  Data pointers are fake (never dereferenced on the host).  Also
+checks that libra.so exports every function include/ra.h declares.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+RA_OK, RA_E_INVALID, RA_E_UNSUPPORTED, RA_E_ALIGN, RA_E_HIP, RA_E_WORKSPACE = range(6)
+FAKE = 0x10000000  # 16-byte aligned, never dereferenced
+
+
+def _L():
+    from ring_blockwise_softmax_amd import _lib
+    return _lib
+
+
+def T(b, s, h, d, dtype=0, data=FAKE, strides=None):
+    L = _L()
+    if strides is None:
+        strides = (s * h * d, h * d, d)
+    return L.RaTensor(data, dtype, 0, b, s, h, d, *strides)
+
+
+def LSE(b, s, h, data=FAKE, dtype=1):
+    L = _L()
+    return L.RaTensor(data, dtype, 0, b, s, h, 1, h * s, 1, s)
+
+
+def attn(q, k, v, mask, out, lse):
+    L = _L()
+    return L.lib().ra_block_attn_fwd(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), mask,
+                                     ctypes.byref(out), ctypes.byref(lse), None, 0, None)
+
+
+def good(d=128, dtype=0, Sq=64, Sk=64, Hq=4, Hkv=2):
+    return (T(1, Sq, Hq, d, dtype), T(1, Sk, Hkv, d, dtype), T(1, Sk, Hkv, d, dtype),
+            T(1, Sq, Hq, d, 1), LSE(1, Sq, Hq))
+
+
+def test_exports_match_header():
+    L = _L()
+    lib = L.lib()
+    with open(os.path.join(ROOT, "include", "ra.h")) as f:
+        text = f.read()
+    declared = set(re.findall(r"^[A-Za-z_][\w \*]*?\b(ra_\w+)\s*\(", text, flags=re.M))
+    assert {"ra_block_attn_fwd", "ra_merge", "ra_ring_forward", "ra_ring_plan"} <= declared
+    for name in declared:
+        assert hasattr(lib, name), f"libra.so does not export {name}"
+    assert declared <= set(L.EXPORTS), "binding is missing a declared entry point"
+    assert lib.ra_version() == 1
+
+
+def test_status_strings():
+    lib = _L().lib()
+    assert lib.ra_status_str(0) == b"RA_OK"
+    assert lib.ra_status_str(5) == b"RA_E_WORKSPACE"
+
+
+@pytest.mark.parametrize("mutate,status", [
+    (lambda a: a[0].__setattr__("dtype", 7), RA_E_UNSUPPORTED),         # unknown dtype
+    (lambda a: [t.__setattr__("d", 96) for t in a[:3]], RA_E_UNSUPPORTED),  # head_dim 96
+    (lambda a: a[1].__setattr__("h", 3) or a[2].__setattr__("h", 3), RA_E_INVALID),  # Hq % Hkv
+    (lambda a: a[0].__setattr__("data", None), RA_E_INVALID),           # null pointer
+    (lambda a: a[0].__setattr__("data", FAKE + 2), RA_E_ALIGN),         # misaligned
+    (lambda a: a[1].__setattr__("ss", 260), RA_E_ALIGN),                 # stride not 16 B
+    (lambda a: a[1].__setattr__("dtype", 1), RA_E_INVALID),             # mixed dtypes
+    (lambda a: a[3].__setattr__("dtype", 0), RA_E_UNSUPPORTED),         # bf16 out
+    (lambda a: a[3].__setattr__("s", 63), RA_E_INVALID),                 # out shape
+    (lambda a: a[4].__setattr__("h", 2), RA_E_INVALID),                  # lse shape
+    (lambda a: a[4].__setattr__("data", FAKE + 2), RA_E_ALIGN),         # lse alignment
+    (lambda a: a[2].__setattr__("s", 32), RA_E_INVALID),                 # k/v length differ
+    (lambda a: a[1].__setattr__("b", 2), RA_E_INVALID),                  # batch mismatch
+])
+def test_block_attn_rejects(mutate, status):
+    args = list(good())
+    mutate(args)
+    q, k, v, out, lse = args
+    assert attn(q, k, v, 0, out, lse) == status
+    assert _L().lib().ra_last_error()
+
+
+def test_block_attn_rejects_mask():
+    q, k, v, out, lse = good()
+    assert attn(q, k, v, 3, out, lse) == RA_E_INVALID
+    q, k, v, out, lse = good(Sq=80, Sk=64)
+    assert attn(q, k, v, 2, out, lse) == RA_E_INVALID   # bottom-right needs Sq <= Sk
+
+
+def test_empty_query_block_is_a_noop():
+    q, k, v, out, lse = good(Sq=0)
+    q.data = out.data = lse.data = None
+    assert attn(q, k, v, 0, out, lse) == RA_OK
+
+
+def _ring(q, k, v, P, kind, fuse, out, lse, ws=None, ws_bytes=0, rank=-1):
+    L = _L()
+    lay = L.RaLayout(kind, 0, rank, fuse, ws, ws_bytes)
+    return L.lib().ra_ring_forward(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), P, ctypes.byref(lay),
+                                   ctypes.byref(out), ctypes.byref(lse), None)
+
+
+def test_ring_rejects():
+    q, k, v, out, lse = good(Sq=96, Sk=96)
+    assert _ring(q, k, v, 5, 0, 1, out, lse) == RA_E_INVALID        # 96 % 5
+    assert _ring(q, k, v, 5, 2, 1, out, lse) == RA_E_INVALID        # 96 % 10
+    assert _ring(q, k, v, 0, 0, 1, out, lse) == RA_E_UNSUPPORTED
+    assert _ring(q, k, v, 17, 0, 1, out, lse) == RA_E_UNSUPPORTED
+    assert _ring(q, k, v, 4, 9, 1, out, lse) == RA_E_INVALID        # layout kind
+    assert _ring(q, k, v, 4, 0, 1, out, lse, rank=4) == RA_E_INVALID
+    # unfused needs workspace; too small or missing is reported, nothing runs
+    assert _ring(q, k, v, 4, 0, 0, out, lse) == RA_E_WORKSPACE
+    assert _ring(q, k, v, 4, 0, 0, out, lse, ws=FAKE, ws_bytes=100) == RA_E_WORKSPACE
+    q2, k2, v2, out2, lse2 = good(Sq=1, Sk=96)
+    assert _ring(q2, k2, v2, 4, 0, 1, out2, lse2) == RA_E_INVALID   # Sq != Sk for a ring layout
+
+
+def test_workspace_queries():
+    L = _L()
+    lib = L.lib()
+    q, k, v, out, lse = good(Sq=24000, Sk=24000, Hq=32, Hkv=32)
+    fused = L.RaLayout(0, 0, -1, 1, None, 0)
+    unfused = L.RaLayout(0, 0, -1, 0, None, 0)
+    assert lib.ra_ring_workspace_bytes(ctypes.byref(q), ctypes.byref(k), 4, ctypes.byref(fused)) == 0
+    n = lib.ra_ring_workspace_bytes(ctypes.byref(q), ctypes.byref(k), 4, ctypes.byref(unfused))
+    assert n >= 24000 * 32 * 129 * 4
+    # decode shape: split-K partials need scratch
+    q = T(16, 1, 32, 128)
+    k = T(16, 262144, 1, 128)
+    assert lib.ra_block_attn_workspace_bytes(ctypes.byref(q), ctypes.byref(k)) > 0
+
+
+def test_merge_rejects():
+    L = _L()
+    lib = L.lib()
+    out, bout = T(1, 10, 2, 128, 1), T(1, 10, 2, 128, 1, data=FAKE + 0x100000)
+    lse, blse = LSE(1, 10, 2), LSE(1, 10, 2, data=FAKE + 0x200000)
+    bad = T(1, 11, 2, 128, 1, data=FAKE + 0x100000)
+    assert lib.ra_merge(ctypes.byref(out), ctypes.byref(lse), ctypes.byref(bad), ctypes.byref(blse), None) == RA_E_INVALID
+    assert lib.ra_merge(ctypes.byref(out), ctypes.byref(lse), ctypes.byref(out), ctypes.byref(blse), None) == RA_E_INVALID
+    b16 = T(1, 10, 2, 128, 0, data=FAKE + 0x100000)
+    assert lib.ra_merge(ctypes.byref(out), ctypes.byref(lse), ctypes.byref(b16), ctypes.byref(blse), None) == RA_E_UNSUPPORTED
