@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -129,11 +130,25 @@ struct ProfScope {
 // Work tables
 // ---------------------------------------------------------------------------
 struct Geometry {
-  int QT, KT;
+  int QT, KT, nb;
 };
 
-Geometry geometry(int dtype) {
-  return dtype == RA_BF16 ? Geometry{kQTileBF16, kKTileBF16} : Geometry{kQTileF32, kKTileF32};
+// 32-row query blocks per wave of the bf16 kernel for long query blocks.
+// RA_BF16_NB (1 or 2) overrides the default; used for tuning sweeps only.
+int bf16_nb_default() {
+  static int nb = [] {
+    const char *e = getenv("RA_BF16_NB");
+    const int v = e ? atoi(e) : 1;
+    return (v == 2) ? 2 : 1;
+  }();
+  return nb;
+}
+
+// Tile geometry for a launch whose longest item has `rows` packed query rows.
+Geometry geometry(int dtype, int64_t rows = 0) {
+  if (dtype != RA_BF16) return Geometry{kQTileF32, kKTileF32, 1};
+  const int nb = rows > kQTileBF16 ? bf16_nb_default() : 1;
+  return Geometry{kQTileBF16 * nb, kKTileBF16, nb};
 }
 
 void fill_strides(AttnArgs &a, const ra_tensor *q, const ra_tensor *k, const ra_tensor *v) {
@@ -227,8 +242,8 @@ size_t split_bytes(const Split &s, int64_t B, int64_t H, int64_t rows, int64_t D
 // item alone cannot fill the chip and scratch is available.  The result is
 // written (mode kWrite) or merged (kMerge) into the destination held in `a`.
 ra_status run_single_item(AttnArgs a, int dtype, int D, char *ws, size_t ws_bytes, void *stream) {
-  const Geometry geo = geometry(dtype);
   KItem &it = a.items[0];
+  const Geometry geo = geometry(dtype, (int64_t)it.q_len * a.GP);
   const int64_t nqt = (int64_t(it.q_len) * a.GP + geo.QT - 1) / geo.QT;
   const int64_t wgs = (int64_t)a.B * (a.Hq / a.GP) * nqt;
   Split sp = (it.nseg == 1) ? choose_split(wgs, it.seg[0].kv_len, geo.KT) : Split{};
@@ -238,7 +253,7 @@ ra_status run_single_item(AttnArgs a, int dtype, int D, char *ws, size_t ws_byte
     finish_tiles(a, geo.QT);
     if (a.n_work == 0) return RA_OK;
     ProfScope ps(RA_KERNEL_ATTN, stream);
-    const int rc = launch_attn(a, dtype, D, stream);
+    const int rc = launch_attn(a, dtype, D, geo.nb, stream);
     return rc ? hip_fail(rc, "attention launch") : RA_OK;
   }
   it.nsplit = sp.nsplit;
@@ -259,7 +274,7 @@ ra_status run_single_item(AttnArgs a, int dtype, int D, char *ws, size_t ws_byte
   finish_tiles(a, geo.QT);
   {
     ProfScope ps(RA_KERNEL_ATTN, stream);
-    const int rc = launch_attn(a, dtype, D, stream);
+    const int rc = launch_attn(a, dtype, D, geo.nb, stream);
     if (rc) return hip_fail(rc, "attention launch");
   }
   ProfScope ps(RA_KERNEL_SPLIT_REDUCE, stream);
@@ -268,7 +283,7 @@ ra_status run_single_item(AttnArgs a, int dtype, int D, char *ws, size_t ws_byte
 }
 
 size_t single_item_ws(int dtype, int64_t B, int64_t Hq, int GP, int64_t q_len, int64_t kv_len, int64_t D) {
-  const Geometry geo = geometry(dtype);
+  const Geometry geo = geometry(dtype, q_len * GP);
   const int64_t nqt = (q_len * GP + geo.QT - 1) / geo.QT;
   const int64_t wgs = B * (Hq / GP) * nqt;
   return split_bytes(choose_split(wgs, kv_len, geo.KT), B, Hq, q_len, D);
@@ -441,7 +456,6 @@ ra_status ra_ring_forward(const ra_tensor *q, const ra_tensor *k, const ra_tenso
 
   const int D = (int)q->d;
   const int dtype = q->dtype;
-  const Geometry geo = geometry(dtype);
   char *ws = (char *)L->workspace;
   // Block-result workspace (unfused): bout [B][ws_rows][Hq][D], blse [B][Hq][ws_rows].
   float *ws_out = nullptr, *ws_lse = nullptr;
@@ -460,7 +474,8 @@ ra_status ra_ring_forward(const ra_tensor *q, const ra_tensor *k, const ra_tenso
   fill_strides(base, q, k, v);
   int64_t qlen_max = 0;
   for (auto &p : rs.items) qlen_max = std::max(qlen_max, p.q_len);
-  base.GP = choose_gp(qlen_max, base.G, geo.QT);
+  base.GP = choose_gp(qlen_max, base.G, geometry(dtype).QT);
+  const Geometry geo = geometry(dtype, qlen_max * base.GP);
 
   for (int t = 0; t < P; ++t) {
     std::vector<ra_plan_item> step;
@@ -508,7 +523,7 @@ ra_status ra_ring_forward(const ra_tensor *q, const ra_tensor *k, const ra_tenso
         finish_tiles(a, geo.QT);
         if (a.n_work > 0) {
           ProfScope ps(RA_KERNEL_ATTN, stream);
-          const int rc = launch_attn(a, dtype, D, stream);
+          const int rc = launch_attn(a, dtype, D, geo.nb, stream);
           if (rc) return hip_fail(rc, "attention launch");
         }
       }

@@ -191,22 +191,48 @@ __device__ __forceinline__ void epilogue(const AttnArgs &a, const KItem &it, con
 // ---------------------------------------------------------------------------
 // bf16 kernel
 // ---------------------------------------------------------------------------
+// One work-group = 4 waves, each owning 32 packed query rows (QT = 128).
+// Keys advance in 32-key tiles held in a ring of three LDS buffers (K and V
+// each).  Tiles are copied straight from global memory into LDS with
+// global_load_lds_dwordx4 (no staging registers), two tiles ahead of use,
+// with one barrier per tile.  The loop is software-pipelined by one tile:
+// while the VALUs turn S(j) into probabilities, the matrix cores already
+// compute S(j+1) = K(j+1) Q^T.
+//
+// LDS rows are unpadded (2*D bytes) with the 16-byte chunks of each row
+// permuted by an XOR swizzle, chosen so that both the K operand reads (16
+// rows x 16 B per group of 16 lanes) and the V transpose reads (4 rows x
+// 64 B per half-wave) hit 64 distinct banks.
 template <int D>
 struct Bf16Cfg {
-  static constexpr int KT = kKTileBF16;          // keys per LDS tile
-  static constexpr int QT = kQTileBF16;          // packed rows per work-group
-  static constexpr int LD = D + 8;               // LDS row pitch (elements)
-  static constexpr int CHUNKS = KT * D / 8;      // 16-byte chunks per K (or V) tile
-  static constexpr int CPT = CHUNKS / kThreads;  // chunks per thread
-  static constexpr int TILE_ELEMS = KT * LD;
-  static constexpr size_t LDS_BYTES = 2 /*K,V*/ * 2 /*buffers*/ * TILE_ELEMS * sizeof(bf16);
+  static constexpr int KT = kKTileBF16;               // keys per LDS tile (32)
+  static constexpr int QT = kQTileBF16;               // packed rows per work-group
+  static constexpr int NBUF = 3;
+  static constexpr int ROWB = 2 * D;                  // bytes per LDS row
+  static constexpr int TILE_BYTES = KT * ROWB;        // one tensor, one tile
+  static constexpr int BUF_BYTES = 2 * TILE_BYTES;    // K then V
+  static constexpr size_t LDS_BYTES = NBUF * BUF_BYTES;
+  static constexpr int BLOCKS = TILE_BYTES / 1024;    // 1 KB direct-load blocks per tensor tile
+  static constexpr int CPT = BLOCKS / 4;              // blocks per wave
+  static constexpr int RPB = 1024 / ROWB;             // rows per block
+  static constexpr int CH = D / 8;                    // 16-byte chunks per row
+  static_assert(CPT >= 1, "tile too small for four waves");
+  __device__ static int swz(int r) {
+    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  }
+  // Byte offset of element e (a multiple of 4 inside one chunk) of row r.
+  __device__ static int off(int r, int e) { return r * ROWB + ((((e >> 3) ^ swz(r)) << 4) | ((e & 7) << 1)); }
 };
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(const AttnArgs a) {
   using C = Bf16Cfg<D>;
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-  bf16 *smem = reinterpret_cast<bf16 *>(smem_raw);
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[];
+  lds_u8 *lds = (lds_u8 *)smem_raw;
 
   Tile t;
   if (!decode_tile(a, t)) return;
@@ -214,7 +240,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(const AttnArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int n = lane & 31;  // query column of this lane
   const int g = lane >> 5;  // lane half
   const int i16 = lane & 15, G16 = lane >> 4;
@@ -225,28 +251,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(const AttnArgs a) {
   const int prow = wave_row0 + n;
   const bool row_ok = prow < rows_total;
   const int hkv = (t.hb * a.GP) / a.G;
-
-  // Positions of this lane's query, of the wave's rows and of the tile's rows.
   const int qpos = it.qpos0 + (row_ok ? prow : rows_total - 1) / a.GP;
-  const int wave_last = min(wave_row0 + 31, rows_total - 1);
   const int wave_qpos_min = it.qpos0 + min(wave_row0, rows_total - 1) / a.GP;
-  const int wave_qpos_max = it.qpos0 + wave_last / a.GP;
-  const bool wave_active = wave_row0 < rows_total;
   const int tile_qpos_max = it.qpos0 + (min(tile_row0 + C::QT, rows_total) - 1) / a.GP;
 
   // Q fragment (B operand of S^T = K Q^T): d = 16*kc + 8*g + 0..7.
   bf16x8 qf[D / 16];
   {
-    const int tok = (row_ok ? prow : 0) / a.GP;
-    const int h = t.hb * a.GP + (row_ok ? prow : 0) % a.GP;
+    const int pr = row_ok ? prow : 0;
+    const int tok = pr / a.GP;
+    const int h = t.hb * a.GP + pr % a.GP;
     const bf16 *qp = reinterpret_cast<const bf16 *>(a.q) + (int64_t)t.b * a.q_sb +
                      (int64_t)(it.q_start + tok) * a.q_ss + (int64_t)h * a.q_sh + 8 * g;
 #pragma unroll
     for (int kc = 0; kc < D / 16; ++kc) {
-      if (row_ok)
-        qf[kc] = *(const bf16x8 *)(qp + 16 * kc);
-      else
-        qf[kc] = bf16x8{};
+      qf[kc] = *(const bf16x8 *)(qp + 16 * kc);
+      if (!row_ok) qf[kc] = bf16x8{};
     }
   }
 
@@ -257,162 +277,162 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(const AttnArgs a) {
   float l_part = 0.0f;
 
   // Key tiles of the (up to two) segments, flattened.
-  SegRange sr0 = seg_range(it, 0, t.split, tile_qpos_max);
-  SegRange sr1 = sr0;
-  int nt0 = (sr0.hi - sr0.lo + C::KT - 1) / C::KT;
-  int nt1 = 0;
-  if (it.nseg > 1) {
-    sr1 = seg_range(it, 1, t.split, tile_qpos_max);
-    nt1 = (sr1.hi - sr1.lo + C::KT - 1) / C::KT;
-  }
+  const SegRange sr0 = seg_range(it, 0, t.split, tile_qpos_max);
+  const SegRange sr1 = it.nseg > 1 ? seg_range(it, 1, t.split, tile_qpos_max) : sr0;
+  const int nt0 = (sr0.hi - sr0.lo + C::KT - 1) / C::KT;
+  const int nt1 = it.nseg > 1 ? (sr1.hi - sr1.lo + C::KT - 1) / C::KT : 0;
   const int ntiles = nt0 + nt1;
 
   const bf16 *kbase = reinterpret_cast<const bf16 *>(a.k) + (int64_t)t.b * a.k_sb + (int64_t)hkv * a.k_sh;
   const bf16 *vbase = reinterpret_cast<const bf16 *>(a.v) + (int64_t)t.b * a.v_sb + (int64_t)hkv * a.v_sh;
 
-  bf16x8 kreg[C::CPT], vreg[C::CPT];
-
-  auto tile_info = [&](int ti, SegRange &sr, int &key0) {
-    if (ti < nt0) {
-      sr = sr0;
-      key0 = sr0.lo + ti * C::KT;
-    } else {
-      sr = sr1;
-      key0 = sr1.lo + (ti - nt0) * C::KT;
-    }
-  };
-
-  auto gload = [&](int ti) {
-    SegRange sr;
-    int key0;
-    tile_info(ti, sr, key0);
-    const int nvalid = sr.hi - key0;
+  // Direct-load geometry: block u of this wave covers tile rows
+  // (wave*CPT + u)*RPB + lane/CH; lane writes physical chunk lane%CH, which
+  // holds logical chunk (lane%CH) ^ swz(row).
+  int ld_row[C::CPT], ld_col[C::CPT];
 #pragma unroll
-    for (int u = 0; u < C::CPT; ++u) {
-      const int c = tid + kThreads * u;
-      const int key = c / (D / 8);
-      const int col = (c % (D / 8)) * 8;
-      if (key < nvalid) {
-        const int64_t row = sr.kv_start + key0 + key;
-        kreg[u] = *(const bf16x8 *)(kbase + row * a.k_ss + col);
-        vreg[u] = *(const bf16x8 *)(vbase + row * a.v_ss + col);
-      } else {
-        kreg[u] = bf16x8{};
-        vreg[u] = bf16x8{};
-      }
-    }
-  };
-
-  auto lstore = [&](int buf) {
-    bf16 *Ks = smem + buf * 2 * C::TILE_ELEMS;
-    bf16 *Vs = Ks + C::TILE_ELEMS;
-#pragma unroll
-    for (int u = 0; u < C::CPT; ++u) {
-      const int c = tid + kThreads * u;
-      const int key = c / (D / 8);
-      const int col = (c % (D / 8)) * 8;
-      *(bf16x8 *)(Ks + key * C::LD + col) = kreg[u];
-      *(bf16x8 *)(Vs + key * C::LD + col) = vreg[u];
-    }
-  };
-
-  if (ntiles > 0) {
-    gload(0);
-    lstore(0);
+  for (int u = 0; u < C::CPT; ++u) {
+    const int blk = wave * C::CPT + u;
+    ld_row[u] = blk * C::RPB + lane / C::CH;
+    ld_col[u] = (((lane % C::CH) ^ C::swz(ld_row[u])) * 8);
   }
-  __syncthreads();
 
-  for (int ti = 0; ti < ntiles; ++ti) {
-    const int buf = ti & 1;
-    if (ti + 1 < ntiles) gload(ti + 1);
+  // LDS read offsets (bytes, relative to a buffer): K operand for each kc,
+  // V transpose operand for each (mb, second 8-row half).
+  int koff[D / 16], voff[D / 32][2];
+#pragma unroll
+  for (int kc = 0; kc < D / 16; ++kc) koff[kc] = C::off(n, 16 * kc + 8 * g);
+#pragma unroll
+  for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+      voff[mb][s2] = C::TILE_BYTES +
+                     C::off(4 * g + (i16 >> 2) + 8 * s2, 32 * mb + 16 * (G16 & 1) + 4 * (i16 & 3));
 
+  auto tile_at = [&](int ti, SegRange &sr, int &key0) {
+    sr = ti < nt0 ? sr0 : sr1;
+    key0 = sr.lo + (ti < nt0 ? ti : ti - nt0) * C::KT;
+  };
+
+  // Copy tile ti (K and V) into LDS buffer `buf`.  Rows past the valid range
+  // are clamped to the last valid row (finite data, masked in the softmax).
+  auto issue_load = [&](int ti, int buf) {
     SegRange sr;
     int key0;
-    tile_info(ti, sr, key0);
-    const bf16 *Ks = smem + buf * 2 * C::TILE_ELEMS;
-    const bf16 *Vs = Ks + C::TILE_ELEMS;
+    tile_at(ti, sr, key0);
+    const int nvalid = sr.hi - key0;
+    const bf16 *kt = kbase + (int64_t)(sr.kv_start + key0) * a.k_ss;
+    const bf16 *vt = vbase + (int64_t)(sr.kv_start + key0) * a.v_ss;
+#pragma unroll
+    for (int u = 0; u < C::CPT; ++u) {
+      const int row = min(ld_row[u], nvalid - 1);
+      const int blk = wave * C::CPT + u;
+      __builtin_amdgcn_global_load_lds((const void *)(kt + row * (int)a.k_ss + ld_col[u]),
+                                       (lds_void *)(lds + buf * C::BUF_BYTES + blk * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void *)(vt + row * (int)a.v_ss + ld_col[u]),
+                                       (lds_void *)(lds + buf * C::BUF_BYTES + C::TILE_BYTES + blk * 1024), 16, 0, 0);
+    }
+  };
 
+  auto s_mfma = [&](int buf, f32x16 &s, int kc0, int kc1) {
 #pragma unroll
-    for (int sub = 0; sub < C::KT / 32; ++sub) {
-      const int kb = key0 + sub * 32;  // first key of this sub-tile (segment-local)
-      // Wave-uniform skip: no rows, no valid keys, or every key after every row.
-      const bool skip = !wave_active || kb >= sr.hi ||
-                        (sr.causal && sr.kpos0 + kb > wave_qpos_max);
-      if (skip) continue;
-      const bool need_mask = (kb + 32 > sr.hi) || (sr.causal && sr.kpos0 + kb + 31 > wave_qpos_min);
+    for (int kc = kc0; kc < kc1; ++kc) {
+      const bf16x8 ka = *(const bf16x8 *)(lds + buf * C::BUF_BYTES + koff[kc]);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kc], s, 0, 0, 0);
+    }
+  };
 
-      // S^T = K Q^T for 32 keys x 32 queries.
-      f32x16 s = f32x16{};
+  // Softmax of tile ti (scores in s) interleaved with the S MFMAs of tile
+  // ti+1 (K in buffer bn), then P*V for tile ti (V in buffer bc).
+  auto step = [&](f32x16 &s, int ti, int bc, int bn, f32x16 &s_next) {
+    SegRange sr;
+    int kb;
+    tile_at(ti, sr, kb);
+    const bool need_mask = (kb + 32 > sr.hi) || (sr.causal && sr.kpos0 + kb + 31 > wave_qpos_min);
+    if (need_mask) {
+      // key (segment-local) visible iff key < lim
+      const int lim = sr.causal ? min(sr.hi, qpos - sr.kpos0 + 1) : sr.hi;
+      const int kl = kb + 4 * g;
 #pragma unroll
-      for (int kc = 0; kc < D / 16; ++kc) {
-        const bf16x8 ka = *(const bf16x8 *)(Ks + (sub * 32 + n) * C::LD + 16 * kc + 8 * g);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kc], s, 0, 0, 0);
-      }
-
-      if (need_mask) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kb + 8 * (r >> 2) + 4 * g + (r & 3);
-          const bool vis = key < sr.hi && (!sr.causal || sr.kpos0 + key <= qpos);
-          if (!vis) s[r] = neg_inf();
-        }
-      }
-
-      // Row maximum (log2 domain) and lazy rescale.
-      float mx = s[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-      mx = max_halves(mx) * a.scale_log2;
-      const float m_new = fmaxf(m_run, mx);
-      const bool need = m_new > m_run + kRescaleThreshold;
-      if (__builtin_amdgcn_ballot_w64(need)) {
-        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-        m_run = need ? m_new : m_run;
-        l_part *= alpha;
-#pragma unroll
-        for (int mb = 0; mb < D / 32; ++mb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[mb][r] *= alpha;
-      }
-      const float moff = (m_run == neg_inf()) ? 0.0f : m_run;
-
-      // P = exp2(s * scale_log2 - m).  The row sum takes the fp32 values
-      // (so lse is exact to fp32); the P*V product takes them rounded to
-      // bf16 (round to nearest even).
-      bf16x8 pb[2];
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * c + e], a.scale_log2, -moff));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * c + e + 1], a.scale_log2, -moff));
-          const bf16x2 pp = {(bf16)p0, (bf16)p1};
-          pb[c][e] = pp[0];
-          pb[c][e + 1] = pp[1];
-          l_part += p0 + p1;
-        }
-      }
-
-      // out^T += V^T P^T over two 16-key chunks.
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int krow = sub * 32 + 16 * c + 4 * g + (i16 >> 2);
-#pragma unroll
-        for (int mb = 0; mb < D / 32; ++mb) {
-          const int dcol = 32 * mb + 16 * (G16 & 1) + 4 * (i16 & 3);
-          const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4 *)(Vs + krow * C::LD + dcol));
-          const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4 *)(Vs + (krow + 8) * C::LD + dcol));
-          const s16x8 vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pb[c],
-                                                            acc[mb], 0, 0, 0);
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int key = kl + 8 * (r >> 2) + (r & 3);
+        s[r] = key < lim ? s[r] : neg_inf();
       }
     }
+    s_next = f32x16{};
+    s_mfma(bn, s_next, 0, 2);
+    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+#pragma unroll
+    for (int r = 4; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[r], s[r + 1]));
+    mx = max_halves(mx) * a.scale_log2;
+    const float m_new = fmaxf(m_run, mx);
+    const bool need = m_new > m_run + kRescaleThreshold;
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+      m_run = need ? m_new : m_run;
+      l_part *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[mb][r] *= alpha;
+    }
+    const float moff = (m_run == neg_inf()) ? 0.0f : m_run;
+    s_mfma(bn, s_next, 2, D / 16);
 
-    if (ti + 1 < ntiles) lstore(buf ^ 1);
+    // P = exp2(s * scale_log2 - m): fp32 for the row sum, bf16 (RNE) for P*V.
+    bf16x8 pb[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * c + e], a.scale_log2, -moff));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * c + e + 1], a.scale_log2, -moff));
+        const bf16x2 pp = {(bf16)p0, (bf16)p1};
+        pb[c][e] = pp[0];
+        pb[c][e + 1] = pp[1];
+        l_part += p0 + p1;
+      }
+    }
+    // out^T += V^T P^T over two 16-key chunks (chunk c is 16 rows further).
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+#pragma unroll
+      for (int mb = 0; mb < D / 32; ++mb) {
+        const lds_u8 *vb = lds + bc * C::BUF_BYTES + 16 * c * C::ROWB;
+        const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vb + voff[mb][0]));
+        const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vb + voff[mb][1]));
+        const s16x8 vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pb[c], acc[mb], 0, 0, 0);
+      }
+    }
+  };
+
+  f32x16 s_a = f32x16{}, s_b = f32x16{};
+  if (ntiles > 0) {
+    issue_load(0, 0);
+    if (ntiles > 1) issue_load(1, 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    s_mfma(0, s_a, 0, D / 16);
+  }
+
+  // One pipeline stage: tile ti+1 must have landed (its copy was issued a
+  // stage earlier), every wave must be done with the buffer tile ti+2 will
+  // reuse, then the copy of tile ti+2 starts and tile ti is consumed.
+  auto stage = [&](int ti, int bc, int bn, int bl, f32x16 &s_cur, f32x16 &s_nxt) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (ti + 2 < ntiles) issue_load(ti + 2, bl);
+    step(s_cur, ti, bc, bn, s_nxt);
+  };
+
+  for (int ti = 0; ti < ntiles; ti += 3) {
+    stage(ti, 0, 1, 2, s_a, s_b);
+    if (ti + 1 >= ntiles) break;
+    stage(ti + 1, 1, 2, 0, s_b, s_a);
+    if (ti + 2 >= ntiles) break;
+    stage(ti + 2, 2, 0, 1, s_a, s_b);
+    s_a = s_b;
   }
 
   epilogue<D>(a, it, t, prow, row_ok, acc, m_run, l_part, g);
@@ -725,31 +745,34 @@ static int set_lds(K kernel, size_t bytes, bool &done) {
   return 0;
 }
 
-int launch_attn(const AttnArgs &a, int dtype, int head_dim, void *stream) {
+template <int D>
+static int launch_bf16(const AttnArgs &a, dim3 grid, dim3 block, hipStream_t s) {
+  static bool done = false;
+  const int rc = set_lds(attn_fwd_bf16<D>, Bf16Cfg<D>::LDS_BYTES, done);
+  if (rc) return rc;
+  attn_fwd_bf16<D><<<grid, block, Bf16Cfg<D>::LDS_BYTES, s>>>(a);
+  return 0;
+}
+
+template <int D>
+static int launch_f32(const AttnArgs &a, dim3 grid, dim3 block, hipStream_t s) {
+  static bool done = false;
+  const int rc = set_lds(attn_fwd_f32<D>, F32Cfg<D>::LDS_BYTES, done);
+  if (rc) return rc;
+  attn_fwd_f32<D><<<grid, block, F32Cfg<D>::LDS_BYTES, s>>>(a);
+  return 0;
+}
+
+int launch_attn(const AttnArgs &a, int dtype, int head_dim, int nb, void *stream) {
   const dim3 grid(a.per_xcd * 8), block(kThreads);
   hipStream_t s = (hipStream_t)stream;
-  int rc = 0;
+  int rc;
   if (dtype == 0) {
-    if (head_dim == 128) {
-      static bool done = false;
-      if ((rc = set_lds(attn_fwd_bf16<128>, Bf16Cfg<128>::LDS_BYTES, done))) return rc;
-      hipLaunchKernelGGL(attn_fwd_bf16<128>, grid, block, Bf16Cfg<128>::LDS_BYTES, s, a);
-    } else {
-      static bool done = false;
-      if ((rc = set_lds(attn_fwd_bf16<64>, Bf16Cfg<64>::LDS_BYTES, done))) return rc;
-      hipLaunchKernelGGL(attn_fwd_bf16<64>, grid, block, Bf16Cfg<64>::LDS_BYTES, s, a);
-    }
+    rc = head_dim == 128 ? launch_bf16<128>(a, grid, block, s) : launch_bf16<64>(a, grid, block, s);
   } else {
-    if (head_dim == 128) {
-      static bool done = false;
-      if ((rc = set_lds(attn_fwd_f32<128>, F32Cfg<128>::LDS_BYTES, done))) return rc;
-      hipLaunchKernelGGL(attn_fwd_f32<128>, grid, block, F32Cfg<128>::LDS_BYTES, s, a);
-    } else {
-      static bool done = false;
-      if ((rc = set_lds(attn_fwd_f32<64>, F32Cfg<64>::LDS_BYTES, done))) return rc;
-      hipLaunchKernelGGL(attn_fwd_f32<64>, grid, block, F32Cfg<64>::LDS_BYTES, s, a);
-    }
+    rc = head_dim == 128 ? launch_f32<128>(a, grid, block, s) : launch_f32<64>(a, grid, block, s);
   }
+  if (rc) return rc;
   return (int)hipGetLastError();
 }
 
