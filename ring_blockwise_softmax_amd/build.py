@@ -24,8 +24,10 @@ COMMON = [
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 # Device code: gfx950 only; packed fp32 VALU forms are disabled.
+# -fno-honor-nans: no kernel tests for NaN; without it every fmax pays a
+# NaN-quieting canonicalisation.
 DEVICE = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-munsafe-fp-atomics"]
+          "-fno-honor-nans"]
 
 
 def hipcc() -> str:

@@ -130,25 +130,26 @@ struct ProfScope {
 // Work tables
 // ---------------------------------------------------------------------------
 struct Geometry {
-  int QT, KT, nb;
+  int QT, KT, nw;
 };
 
-// 32-row query blocks per wave of the bf16 kernel for long query blocks.
-// RA_BF16_NB (1 or 2) overrides the default; used for tuning sweeps only.
-int bf16_nb_default() {
-  static int nb = [] {
-    const char *e = getenv("RA_BF16_NB");
-    const int v = e ? atoi(e) : 1;
-    return (v == 2) ? 2 : 1;
+// Waves per work-group of the bf16 kernel (32 query rows each).
+// RA_BF16_WAVES (4 or 8) overrides the default; used for tuning sweeps only.
+int bf16_waves() {
+  static int nw = [] {
+    const char *e = getenv("RA_BF16_WAVES");
+    const int v = e ? atoi(e) : 4;
+    return (v == 8) ? 8 : 4;
   }();
-  return nb;
+  return nw;
 }
 
-// Tile geometry for a launch whose longest item has `rows` packed query rows.
+// Tile geometry of the attention kernel for a dtype.
 Geometry geometry(int dtype, int64_t rows = 0) {
-  if (dtype != RA_BF16) return Geometry{kQTileF32, kKTileF32, 1};
-  const int nb = rows > kQTileBF16 ? bf16_nb_default() : 1;
-  return Geometry{kQTileBF16 * nb, kKTileBF16, nb};
+  (void)rows;
+  if (dtype != RA_BF16) return Geometry{kQTileF32, kKTileF32, 4};
+  const int nw = bf16_waves();
+  return Geometry{32 * nw, kKTileBF16, nw};
 }
 
 void fill_strides(AttnArgs &a, const ra_tensor *q, const ra_tensor *k, const ra_tensor *v) {
@@ -173,7 +174,7 @@ void set_dest(AttnArgs &a, float *out, int64_t o_sb, int64_t o_ss, int64_t o_sh,
 
 // Packing of grouped query heads into tile rows: when the query block is
 // shorter than a tile, the heads sharing one K/V head are packed as rows.
-int choose_gp(int64_t q_len_max, int G, int QT) { return (q_len_max * 1 < QT && G > 1) ? G : 1; }
+int choose_gp(int64_t q_len_max, int G, int QT) { return (q_len_max < QT && G > 1) ? G : 1; }
 
 // Finalise tile counts and XCD split after items are filled in.
 void finish_tiles(AttnArgs &a, int QT) {
@@ -253,7 +254,7 @@ ra_status run_single_item(AttnArgs a, int dtype, int D, char *ws, size_t ws_byte
     finish_tiles(a, geo.QT);
     if (a.n_work == 0) return RA_OK;
     ProfScope ps(RA_KERNEL_ATTN, stream);
-    const int rc = launch_attn(a, dtype, D, geo.nb, stream);
+    const int rc = launch_attn(a, dtype, D, geo.nw, stream);
     return rc ? hip_fail(rc, "attention launch") : RA_OK;
   }
   it.nsplit = sp.nsplit;
@@ -274,7 +275,7 @@ ra_status run_single_item(AttnArgs a, int dtype, int D, char *ws, size_t ws_byte
   finish_tiles(a, geo.QT);
   {
     ProfScope ps(RA_KERNEL_ATTN, stream);
-    const int rc = launch_attn(a, dtype, D, geo.nb, stream);
+    const int rc = launch_attn(a, dtype, D, geo.nw, stream);
     if (rc) return hip_fail(rc, "attention launch");
   }
   ProfScope ps(RA_KERNEL_SPLIT_REDUCE, stream);
@@ -523,7 +524,7 @@ ra_status ra_ring_forward(const ra_tensor *q, const ra_tensor *k, const ra_tenso
         finish_tiles(a, geo.QT);
         if (a.n_work > 0) {
           ProfScope ps(RA_KERNEL_ATTN, stream);
-          const int rc = launch_attn(a, dtype, D, geo.nb, stream);
+          const int rc = launch_attn(a, dtype, D, geo.nw, stream);
           if (rc) return hip_fail(rc, "attention launch");
         }
       }

@@ -51,6 +51,26 @@ constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
+// Work-group barrier without a memory fence.  __syncthreads() adds a release
+// fence, which waits for every outstanding global access, including LDS
+// copies still in flight for later tiles.  The pipelines below order their
+// LDS traffic themselves (explicit vmcnt waits for the tile being published;
+// every read of a recycled buffer is consumed before the barrier); the
+// memory clobber keeps the compiler from moving accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// 16 bytes per lane from global memory straight into LDS: lane i's bytes land
+// at lds_addr + 16*i.  Written as inline asm so that the compiler does not
+// track these copies and wait for them before unrelated LDS reads; the
+// kernels wait for them explicitly (s_waitcnt vmcnt) before publishing a
+// tile.  No register outputs; the address is consumed at issue.
+__device__ __forceinline__ void copy16_to_lds(const void *g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(lds_addr)
+               : "memory", "m0");
+}
+
 // max / sum of a value with its partner lane in the other half of the wave.
 __device__ __forceinline__ float max_halves(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
@@ -191,32 +211,37 @@ __device__ __forceinline__ void epilogue(const AttnArgs &a, const KItem &it, con
 // ---------------------------------------------------------------------------
 // bf16 kernel
 // ---------------------------------------------------------------------------
-// One work-group = 4 waves, each owning 32 packed query rows (QT = 128).
-// Keys advance in 32-key tiles held in a ring of three LDS buffers (K and V
-// each).  Tiles are copied straight from global memory into LDS with
-// global_load_lds_dwordx4 (no staging registers), two tiles ahead of use,
-// with one barrier per tile.  The loop is software-pipelined by one tile:
-// while the VALUs turn S(j) into probabilities, the matrix cores already
-// compute S(j+1) = K(j+1) Q^T.
+// One work-group = NW waves (4 or 8), each owning 32 packed query rows
+// (QT = 32*NW).  Keys advance in 32-key tiles held in a ring of four LDS
+// buffers (K and V each).  Tiles are copied straight from global memory into
+// LDS with global_load_lds_dwordx4 (no staging registers), three tiles ahead
+// of use, with one barrier per tile.  The four buffers are distinct LDS
+// objects: that lets the compiler see that reads of one buffer do not alias
+// the copies in flight into another, so it does not wait for those copies.
+// The loop is software-pipelined by one tile: while the VALUs turn S(j) into
+// probabilities, the matrix cores already compute S(j+1) = K(j+1) Q^T.
 //
 // LDS rows are unpadded (2*D bytes) with the 16-byte chunks of each row
 // permuted by an XOR swizzle, chosen so that both the K operand reads (16
 // rows x 16 B per group of 16 lanes) and the V transpose reads (4 rows x
 // 64 B per half-wave) hit 64 distinct banks.
-template <int D>
+template <int D, int NW_, int NBUF_>
 struct Bf16Cfg {
+  static constexpr int NW = NW_;                      // waves per work-group
+  static constexpr int THREADS = 64 * NW;
   static constexpr int KT = kKTileBF16;               // keys per LDS tile (32)
-  static constexpr int QT = kQTileBF16;               // packed rows per work-group
-  static constexpr int NBUF = 3;
+  static constexpr int QT = 32 * NW;                  // packed rows per work-group
+  static constexpr int NBUF = NBUF_;                  // ring of LDS buffers (even)
   static constexpr int ROWB = 2 * D;                  // bytes per LDS row
   static constexpr int TILE_BYTES = KT * ROWB;        // one tensor, one tile
   static constexpr int BUF_BYTES = 2 * TILE_BYTES;    // K then V
-  static constexpr size_t LDS_BYTES = NBUF * BUF_BYTES;
+  static constexpr size_t LDS_BYTES = (size_t)NBUF * BUF_BYTES;
   static constexpr int BLOCKS = TILE_BYTES / 1024;    // 1 KB direct-load blocks per tensor tile
-  static constexpr int CPT = BLOCKS / 4;              // blocks per wave
+  static constexpr int CPW = 2 * BLOCKS / NW;         // blocks (K and V) copied per wave
   static constexpr int RPB = 1024 / ROWB;             // rows per block
   static constexpr int CH = D / 8;                    // 16-byte chunks per row
-  static_assert(CPT >= 1, "tile too small for four waves");
+  static_assert(CPW >= 1 && (2 * BLOCKS) % NW == 0, "tile blocks must split evenly over the waves");
+  static_assert(NBUF >= 4 && NBUF % 2 == 0, "the unrolled loop alternates two score registers");
   __device__ static int swz(int r) {
     if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
     else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
@@ -227,12 +252,15 @@ struct Bf16Cfg {
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 
-template <int D>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(const AttnArgs a) {
-  using C = Bf16Cfg<D>;
+// Two waves per SIMD: 8 / NW work-groups per CU.
+template <int D, int NW, int NBUF>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_bf16(const AttnArgs a) {
+  using C = Bf16Cfg<D, NW, NBUF>;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[];
-  lds_u8 *lds = (lds_u8 *)smem_raw;
+  // Buffer b of the ring (b is a compile-time constant after unrolling).
+  auto bufp = [&](int b) -> lds_u8 * { return (lds_u8 *)smem_raw + b * C::BUF_BYTES; };
 
   Tile t;
   if (!decode_tile(a, t)) return;
@@ -286,15 +314,23 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(const AttnArgs a) {
   const bf16 *kbase = reinterpret_cast<const bf16 *>(a.k) + (int64_t)t.b * a.k_sb + (int64_t)hkv * a.k_sh;
   const bf16 *vbase = reinterpret_cast<const bf16 *>(a.v) + (int64_t)t.b * a.v_sb + (int64_t)hkv * a.v_sh;
 
-  // Direct-load geometry: block u of this wave covers tile rows
-  // (wave*CPT + u)*RPB + lane/CH; lane writes physical chunk lane%CH, which
-  // holds logical chunk (lane%CH) ^ swz(row).
-  int ld_row[C::CPT], ld_col[C::CPT];
+  // Direct-load geometry: this wave copies blocks bi = wave + NW*u of the
+  // tile (K blocks first, then V).  Block b covers tile rows b*RPB ..; lane
+  // writes physical chunk lane%CH of row b*RPB + lane/CH, which holds logical
+  // chunk (lane%CH) ^ swz(row).  Byte offsets are from the tile's first row,
+  // for full tiles (clamped rows are recomputed on partial ones).
+  int ld_row[C::CPW], ld_col[C::CPW], ld_lds[C::CPW];
+  uint32_t ld_off[C::CPW];
+  bool ld_isv[C::CPW];
 #pragma unroll
-  for (int u = 0; u < C::CPT; ++u) {
-    const int blk = wave * C::CPT + u;
+  for (int u = 0; u < C::CPW; ++u) {
+    const int bi = wave + C::NW * u;
+    ld_isv[u] = bi >= C::BLOCKS;
+    const int blk = ld_isv[u] ? bi - C::BLOCKS : bi;
     ld_row[u] = blk * C::RPB + lane / C::CH;
     ld_col[u] = (((lane % C::CH) ^ C::swz(ld_row[u])) * 8);
+    ld_lds[u] = (ld_isv[u] ? C::TILE_BYTES : 0) + blk * 1024;
+    ld_off[u] = (uint32_t)(ld_row[u] * (int)(ld_isv[u] ? a.v_ss : a.k_ss) + ld_col[u]) * 2u;
   }
 
   // LDS read offsets (bytes, relative to a buffer): K operand for each kc,
@@ -321,23 +357,27 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(const AttnArgs a) {
     int key0;
     tile_at(ti, sr, key0);
     const int nvalid = sr.hi - key0;
-    const bf16 *kt = kbase + (int64_t)(sr.kv_start + key0) * a.k_ss;
-    const bf16 *vt = vbase + (int64_t)(sr.kv_start + key0) * a.v_ss;
+    const char *kt = reinterpret_cast<const char *>(kbase + (int64_t)(sr.kv_start + key0) * a.k_ss);
+    const char *vt = reinterpret_cast<const char *>(vbase + (int64_t)(sr.kv_start + key0) * a.v_ss);
+    if (nvalid >= C::KT) {
 #pragma unroll
-    for (int u = 0; u < C::CPT; ++u) {
-      const int row = min(ld_row[u], nvalid - 1);
-      const int blk = wave * C::CPT + u;
-      __builtin_amdgcn_global_load_lds((const void *)(kt + row * (int)a.k_ss + ld_col[u]),
-                                       (lds_void *)(lds + buf * C::BUF_BYTES + blk * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void *)(vt + row * (int)a.v_ss + ld_col[u]),
-                                       (lds_void *)(lds + buf * C::BUF_BYTES + C::TILE_BYTES + blk * 1024), 16, 0, 0);
+      for (int u = 0; u < C::CPW; ++u)
+        copy16_to_lds((const void *)((ld_isv[u] ? vt : kt) + ld_off[u]),
+                      (uint32_t)(uintptr_t)(bufp(buf) + ld_lds[u]));
+    } else {
+#pragma unroll
+      for (int u = 0; u < C::CPW; ++u) {
+        const int row = min(ld_row[u], nvalid - 1);
+        const uint32_t o = (uint32_t)(row * (int)(ld_isv[u] ? a.v_ss : a.k_ss) + ld_col[u]) * 2u;
+        copy16_to_lds((const void *)((ld_isv[u] ? vt : kt) + o), (uint32_t)(uintptr_t)(bufp(buf) + ld_lds[u]));
+      }
     }
   };
 
   auto s_mfma = [&](int buf, f32x16 &s, int kc0, int kc1) {
 #pragma unroll
     for (int kc = kc0; kc < kc1; ++kc) {
-      const bf16x8 ka = *(const bf16x8 *)(lds + buf * C::BUF_BYTES + koff[kc]);
+      const bf16x8 ka = *(const lds_bf16x8 *)(bufp(buf) + koff[kc]);
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kc], s, 0, 0, 0);
     }
   };
@@ -361,9 +401,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(const AttnArgs a) {
     }
     s_next = f32x16{};
     s_mfma(bn, s_next, 0, 2);
-    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    float mx = __builtin_fmaxf(__builtin_fmaxf(s[0], s[1]), s[2]);
 #pragma unroll
-    for (int r = 4; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[r], s[r + 1]));
+    for (int r = 3; r < 15; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s[r]), s[r + 1]);
+    mx = __builtin_fmaxf(mx, s[15]);
     mx = max_halves(mx) * a.scale_log2;
     const float m_new = fmaxf(m_run, mx);
     const bool need = m_new > m_run + kRescaleThreshold;
@@ -398,7 +439,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(const AttnArgs a) {
     for (int c = 0; c < 2; ++c) {
 #pragma unroll
       for (int mb = 0; mb < D / 32; ++mb) {
-        const lds_u8 *vb = lds + bc * C::BUF_BYTES + 16 * c * C::ROWB;
+        const lds_u8 *vb = bufp(bc) + 16 * c * C::ROWB;
         const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vb + voff[mb][0]));
         const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vb + voff[mb][1]));
         const s16x8 vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
@@ -408,31 +449,61 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(const AttnArgs a) {
   };
 
   f32x16 s_a = f32x16{}, s_b = f32x16{};
+  // Tiles are copied PF = NBUF-1 tiles ahead of use.  Copies complete in
+  // order, so "tile j+1 has landed" is "at most (copies issued after it) are
+  // still outstanding": wait_vm(n) waits until at most n copy instructions
+  // per wave remain.
+  constexpr int PF = NBUF - 1;
+  auto wait_vm = [&](int tiles_after) {
+    // at most n = tiles_after * CPW copies may remain; s_waitcnt takes an
+    // immediate, so dispatch on n (never rounding up)
+    const int n = tiles_after * C::CPW;
+    switch (n) {
+      case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+      case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
+      case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+      case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
+      case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+      case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
+      case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+      case 7: asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
+      case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+      case 9: asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); break;
+      case 10: asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
+      case 11: asm volatile("s_waitcnt vmcnt(11)" ::: "memory"); break;
+      case 12: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
+      default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;  // never reached (PF <= 7)
+    }
+  };
+  static_assert((NBUF - 3) * C::CPW <= 12, "wait_vm covers at most 12 outstanding copies");
   if (ntiles > 0) {
-    issue_load(0, 0);
-    if (ntiles > 1) issue_load(1, 1);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    const int npro = min(ntiles, PF);
+    for (int j = 0; j < npro; ++j) issue_load(j, j);
+    // tiles 0 and 1 must be in LDS; later ones may still be in flight
+    wait_vm(max(0, npro - 2));
+    lds_barrier();
     s_mfma(0, s_a, 0, D / 16);
   }
 
-  // One pipeline stage: tile ti+1 must have landed (its copy was issued a
-  // stage earlier), every wave must be done with the buffer tile ti+2 will
-  // reuse, then the copy of tile ti+2 starts and tile ti is consumed.
+  // One pipeline stage for tile ti (buffer bc = ti % NBUF): tile ti+1 (buffer
+  // bn) must have landed; tiles ti+2 .. ti+PF-1 may still be in flight.
+  // After the barrier every wave is done with tile ti-1's buffer (bl), which
+  // receives the copy of tile ti+PF.
   auto stage = [&](int ti, int bc, int bn, int bl, f32x16 &s_cur, f32x16 &s_nxt) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (ti + 2 < ntiles) issue_load(ti + 2, bl);
+    wait_vm(min(PF - 2, max(0, ntiles - 1 - (ti + 1))));
+    lds_barrier();
+    if (ti + PF < ntiles) issue_load(ti + PF, bl);
     step(s_cur, ti, bc, bn, s_nxt);
   };
 
-  for (int ti = 0; ti < ntiles; ti += 3) {
-    stage(ti, 0, 1, 2, s_a, s_b);
-    if (ti + 1 >= ntiles) break;
-    stage(ti + 1, 1, 2, 0, s_b, s_a);
-    if (ti + 2 >= ntiles) break;
-    stage(ti + 2, 2, 0, 1, s_a, s_b);
-    s_a = s_b;
+  for (int ti = 0; ti < ntiles; ti += NBUF) {
+#pragma unroll
+    for (int k = 0; k < NBUF; k += 2) {
+      if (ti + k >= ntiles) break;
+      stage(ti + k, k, (k + 1) % NBUF, (k + NBUF - 1) % NBUF, s_a, s_b);
+      if (ti + k + 1 >= ntiles) break;
+      stage(ti + k + 1, k + 1, (k + 2) % NBUF, k, s_b, s_a);
+    }
   }
 
   epilogue<D>(a, it, t, prow, row_ok, acc, m_run, l_part, g);
@@ -745,12 +816,12 @@ static int set_lds(K kernel, size_t bytes, bool &done) {
   return 0;
 }
 
-template <int D>
-static int launch_bf16(const AttnArgs &a, dim3 grid, dim3 block, hipStream_t s) {
+template <int D, int NW, int NBUF>
+static int launch_bf16(const AttnArgs &a, dim3 grid, hipStream_t s) {
   static bool done = false;
-  const int rc = set_lds(attn_fwd_bf16<D>, Bf16Cfg<D>::LDS_BYTES, done);
+  const int rc = set_lds(attn_fwd_bf16<D, NW, NBUF>, Bf16Cfg<D, NW, NBUF>::LDS_BYTES, done);
   if (rc) return rc;
-  attn_fwd_bf16<D><<<grid, block, Bf16Cfg<D>::LDS_BYTES, s>>>(a);
+  attn_fwd_bf16<D, NW, NBUF><<<grid, dim3(64 * NW), Bf16Cfg<D, NW, NBUF>::LDS_BYTES, s>>>(a);
   return 0;
 }
 
@@ -763,12 +834,15 @@ static int launch_f32(const AttnArgs &a, dim3 grid, dim3 block, hipStream_t s) {
   return 0;
 }
 
-int launch_attn(const AttnArgs &a, int dtype, int head_dim, int nb, void *stream) {
+int launch_attn(const AttnArgs &a, int dtype, int head_dim, int nw, void *stream) {
   const dim3 grid(a.per_xcd * 8), block(kThreads);
   hipStream_t s = (hipStream_t)stream;
   int rc;
   if (dtype == 0) {
-    rc = head_dim == 128 ? launch_bf16<128>(a, grid, block, s) : launch_bf16<64>(a, grid, block, s);
+    if (nw == 8)
+      rc = head_dim == 128 ? launch_bf16<128, 8, 4>(a, grid, s) : launch_bf16<64, 8, 4>(a, grid, s);
+    else
+      rc = head_dim == 128 ? launch_bf16<128, 4, 4>(a, grid, s) : launch_bf16<64, 4, 4>(a, grid, s);
   } else {
     rc = head_dim == 128 ? launch_f32<128>(a, grid, block, s) : launch_f32<64>(a, grid, block, s);
   }
