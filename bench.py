@@ -33,9 +33,36 @@ PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 flop/clk (AMD's "2.5 PF" d
 PEAK_F32_MFMA_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 
-# Measured rocprofv3 PMC traffic of the attention kernel (bytes per launch),
-# or None when not measured for the current kernel build.
-ATTN_TRAFFIC_BYTES = None
+KERNEL_SRC = os.path.join(ROOT, "ring_blockwise_softmax_amd", "csrc", "ra_kernels.hip")
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "attn_bf16_mha24k_traffic.json")
+CALIB_BYTES = 1 << 30
+
+
+def kernel_source_sha256():
+    import hashlib
+
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per attention launch from the committed rocprofv3 record.
+
+    The record holds FETCH_SIZE and WRITE_SIZE of the kernel (KiB per
+    dispatch) and of a plain device copy of CALIB_BYTES, measured with the
+    commands it names.  It only applies to the kernel source it was taken
+    on (SHA-256 of ra_kernels.hip); otherwise the traffic is unknown (None).
+    """
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_sha256() or rec.get("workload") != workload:
+        return None
+    f_fetch = rec["calib_bytes"] / (rec["calib_fetch_kib"] * 1024.0)
+    f_write = rec["calib_bytes"] / (rec["calib_write_kib"] * 1024.0)
+    return (rec["attn_fetch_kib"] * f_fetch + rec["attn_write_kib"] * f_write) * 1024.0
 
 
 def visible_pairs(w, rank=None):
@@ -167,6 +194,8 @@ def main():
     ap.add_argument("--rank", type=int, default=None, help="emulate one rank's share only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-merge", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -242,12 +271,19 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
-            "traffic": ATTN_TRAFFIC_BYTES,
+            "traffic": measured_traffic(w.name),
             "launches_per_step": launches_per_step,
             "avg_launch_ms": round(attn_avg_ms, 4),
             "flops_per_launch": flops_per_launch,
         },
     }
+    if args.calib_copy:
+        src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_merge:
         rec["merge"] = merge_bench()
     if not args.no_cpu_baseline:
