@@ -730,22 +730,22 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
   const float *bop = a.bout + (int64_t)b * a.bo_sb + (int64_t)sr * a.bo_ss + (int64_t)h * a.bo_sh + 4 * d4;
   const float *blp = a.blse + (int64_t)b * a.bl_sb + (int64_t)sr * a.bl_ss + (int64_t)h * a.bl_sh;
 
+  // All four loads are issued before any test, so each thread pays one
+  // memory round trip; the -inf identity cases are resolved with selects.
   const float blse = *blp;
-  if (blse == neg_inf()) return;  // identity
   const float lse = *lp;
   const f32x4 bo = __builtin_nontemporal_load((const f32x4 *)bop);
-  if (lse == neg_inf()) {
-    *(f32x4 *)op = bo;
-    if (d4 == 0) *lp = blse;
-    return;
-  }
-  const float diff = blse - lse;
+  const f32x4 o = *(const f32x4 *)op;
+  const bool block_empty = blse == neg_inf();
+  const bool run_empty = lse == neg_inf();
+  const float diff = blse - lse;  // used only when both are finite
   const float w = 1.0f / (1.0f + __expf(-diff));
-  f32x4 o = *(const f32x4 *)op;
+  f32x4 r;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) o[j] = o[j] - w * (o[j] - bo[j]);
-  *(f32x4 *)op = o;
-  if (d4 == 0) *lp = fmaxf(lse, blse) + log1pf(__expf(-fabsf(diff)));
+  for (int j = 0; j < 4; ++j) r[j] = block_empty ? o[j] : (run_empty ? bo[j] : o[j] - w * (o[j] - bo[j]));
+  *(f32x4 *)op = r;
+  if (d4 == 0)
+    *lp = block_empty ? lse : (run_empty ? blse : fmaxf(lse, blse) + log1pf(__expf(-fabsf(diff))));
 }
 
 // ---------------------------------------------------------------------------
@@ -764,23 +764,37 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const SplitArgs a) {
   const int h = (int)(rest % a.H);
   const int b = (int)(rest / a.H);
 
+  // Partials are folded in split order with the sigma rule; loads are issued
+  // eight splits at a time so the fold waits on few memory round trips.
+  constexpr int kChunk = 8;
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
   float l = neg_inf();
-  for (int s = 0; s < a.nsplit; ++s) {
-    const int64_t pr = ((int64_t)(s * a.B + b) * a.H + h) * a.rows + tok;
-    const float bl = a.part_lse[pr];
-    if (bl == neg_inf()) continue;
-    const f32x4 bo = *(const f32x4 *)(a.part_out + pr * a.D + 4 * d4);
-    if (l == neg_inf()) {
-      o = bo;
-      l = bl;
-      continue;
-    }
-    const float diff = bl - l;
-    const float w = 1.0f / (1.0f + __expf(-diff));
+  const int64_t split_stride = (int64_t)a.B * a.H * a.rows;
+  const int64_t pr0 = ((int64_t)b * a.H + h) * a.rows + tok;
+  for (int s0 = 0; s0 < a.nsplit; s0 += kChunk) {
+    float bl[kChunk];
+    f32x4 bo[kChunk];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) o[j] = o[j] - w * (o[j] - bo[j]);
-    l = fmaxf(l, bl) + log1pf(__expf(-fabsf(diff)));
+    for (int j = 0; j < kChunk; ++j) {
+      const int s = min(s0 + j, a.nsplit - 1);
+      const int64_t pr = pr0 + s * split_stride;
+      bl[j] = a.part_lse[pr];
+      bo[j] = *(const f32x4 *)(a.part_out + pr * a.D + 4 * d4);
+    }
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) {
+      if (s0 + j >= a.nsplit || bl[j] == neg_inf()) continue;
+      if (l == neg_inf()) {
+        o = bo[j];
+        l = bl[j];
+        continue;
+      }
+      const float diff = bl[j] - l;
+      const float w = 1.0f / (1.0f + __expf(-diff));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = o[e] - w * (o[e] - bo[j][e]);
+      l = fmaxf(l, bl[j]) + log1pf(__expf(-fabsf(diff)));
+    }
   }
 
   const int orow = a.o_row0 + tok;
