@@ -350,29 +350,64 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_bf16(const AttnArgs 
     key0 = sr.lo + (ti < nt0 ? ti : ti - nt0) * C::KT;
   };
 
-  // Copy tile ti (K and V) into LDS buffer `buf`.  Rows past the valid range
-  // are clamped to the last valid row (finite data, masked in the softmax).
-  auto issue_load = [&](int ti, int buf) {
-    SegRange sr;
-    int key0;
-    tile_at(ti, sr, key0);
-    const int nvalid = sr.hi - key0;
-    const char *kt = reinterpret_cast<const char *>(kbase + (int64_t)(sr.kv_start + key0) * a.k_ss);
-    const char *vt = reinterpret_cast<const char *>(vbase + (int64_t)(sr.kv_start + key0) * a.v_ss);
+  // Copy cursor: tile cp_ti is copied next; cpk/cpv point at its first K/V
+  // row and advance one tile per copy (switching segment once), so the
+  // steady state needs no 64-bit address arithmetic.
+  const int64_t kstep = (int64_t)C::KT * a.k_ss * 2, vstep = (int64_t)C::KT * a.v_ss * 2;
+  const char *kseg1 = reinterpret_cast<const char *>(kbase + (int64_t)(sr1.kv_start + sr1.lo) * a.k_ss);
+  const char *vseg1 = reinterpret_cast<const char *>(vbase + (int64_t)(sr1.kv_start + sr1.lo) * a.v_ss);
+  const char *cpk = reinterpret_cast<const char *>(kbase + (int64_t)(sr0.kv_start + sr0.lo) * a.k_ss);
+  const char *cpv = reinterpret_cast<const char *>(vbase + (int64_t)(sr0.kv_start + sr0.lo) * a.v_ss);
+  if (nt0 == 0) {  // first segment empty in this split
+    cpk = kseg1;
+    cpv = vseg1;
+  }
+  int cp_ti = 0;
+
+  // Copy the next tile (K and V) into LDS buffer `buf` and advance the
+  // cursor.  Rows past the valid range are clamped to the last valid row
+  // (finite data, masked in the softmax).
+  auto issue_next = [&](int buf) {
+    const bool partial = (cp_ti == nt0 - 1) || (cp_ti == ntiles - 1);
+    int nvalid = C::KT;
+    if (partial) {
+      SegRange sr;
+      int key0;
+      tile_at(cp_ti, sr, key0);
+      nvalid = sr.hi - key0;
+    }
     if (nvalid >= C::KT) {
 #pragma unroll
       for (int u = 0; u < C::CPW; ++u)
-        copy16_to_lds((const void *)((ld_isv[u] ? vt : kt) + ld_off[u]),
+        copy16_to_lds((const void *)((ld_isv[u] ? cpv : cpk) + ld_off[u]),
                       (uint32_t)(uintptr_t)(bufp(buf) + ld_lds[u]));
     } else {
 #pragma unroll
       for (int u = 0; u < C::CPW; ++u) {
         const int row = min(ld_row[u], nvalid - 1);
         const uint32_t o = (uint32_t)(row * (int)(ld_isv[u] ? a.v_ss : a.k_ss) + ld_col[u]) * 2u;
-        copy16_to_lds((const void *)((ld_isv[u] ? vt : kt) + o), (uint32_t)(uintptr_t)(bufp(buf) + ld_lds[u]));
+        copy16_to_lds((const void *)((ld_isv[u] ? cpv : cpk) + o), (uint32_t)(uintptr_t)(bufp(buf) + ld_lds[u]));
       }
     }
+    ++cp_ti;
+    if (cp_ti == nt0) {
+      cpk = kseg1;
+      cpv = vseg1;
+    } else {
+      cpk += kstep;
+      cpv += vstep;
+    }
   };
+
+  // Tiles whose segment-local first key kb is at or past these limits need
+  // the per-element mask for this wave (ragged segment end, or keys after
+  // some of this wave's queries under the causal mask).
+  auto first_masked = [&](const SegRange &sr) {
+    int lim = sr.hi - C::KT + 1;
+    if (sr.causal) lim = min(lim, wave_qpos_min - sr.kpos0 - C::KT + 2);
+    return lim;
+  };
+  const int fm0 = first_masked(sr0), fm1 = first_masked(sr1);
 
   auto s_mfma = [&](int buf, f32x16 &s, int kc0, int kc1) {
 #pragma unroll
@@ -385,11 +420,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_bf16(const AttnArgs 
   // Softmax of tile ti (scores in s) interleaved with the S MFMAs of tile
   // ti+1 (K in buffer bn), then P*V for tile ti (V in buffer bc).
   auto step = [&](f32x16 &s, int ti, int bc, int bn, f32x16 &s_next) {
-    SegRange sr;
-    int kb;
-    tile_at(ti, sr, kb);
-    const bool need_mask = (kb + 32 > sr.hi) || (sr.causal && sr.kpos0 + kb + 31 > wave_qpos_min);
-    if (need_mask) {
+    const bool seg1 = ti >= nt0;
+    const int kb = (seg1 ? sr1.lo + (ti - nt0) * C::KT : sr0.lo + ti * C::KT);
+    if (kb >= (seg1 ? fm1 : fm0)) {
+      const SegRange &sr = seg1 ? sr1 : sr0;
       // key (segment-local) visible iff key < lim
       const int lim = sr.causal ? min(sr.hi, qpos - sr.kpos0 + 1) : sr.hi;
       const int kl = kb + 4 * g;
@@ -478,7 +512,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_bf16(const AttnArgs 
   static_assert((NBUF - 3) * C::CPW <= 12, "wait_vm covers at most 12 outstanding copies");
   if (ntiles > 0) {
     const int npro = min(ntiles, PF);
-    for (int j = 0; j < npro; ++j) issue_load(j, j);
+    for (int j = 0; j < npro; ++j) issue_next(j);
     // tiles 0 and 1 must be in LDS; later ones may still be in flight
     wait_vm(max(0, npro - 2));
     lds_barrier();
@@ -486,13 +520,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_bf16(const AttnArgs 
   }
 
   // One pipeline stage for tile ti (buffer bc = ti % NBUF): tile ti+1 (buffer
-  // bn) must have landed; tiles ti+2 .. ti+PF-1 may still be in flight.
-  // After the barrier every wave is done with tile ti-1's buffer (bl), which
-  // receives the copy of tile ti+PF.
+  // bn) must have landed; tiles ti+2 .. ti+PF-1 may still be in flight (in
+  // the last two stages the wait is simply for every copy).  After the
+  // barrier every wave is done with tile ti-1's buffer (bl), which receives
+  // the copy of tile ti+PF.
   auto stage = [&](int ti, int bc, int bn, int bl, f32x16 &s_cur, f32x16 &s_nxt) {
-    wait_vm(min(PF - 2, max(0, ntiles - 1 - (ti + 1))));
+    if (ti + PF - 1 < ntiles)
+      wait_vm(PF - 2);
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();
-    if (ti + PF < ntiles) issue_load(ti + PF, bl);
+    if (ti + PF < ntiles) issue_next(bl);
     step(s_cur, ti, bc, bn, s_nxt);
   };
 
