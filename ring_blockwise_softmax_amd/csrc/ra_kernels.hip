@@ -70,6 +70,14 @@ __device__ __forceinline__ void copy16_to_lds(const void *g, uint32_t lds_addr) 
                : "v"(g), "s"(lds_addr)
                : "memory", "m0");
 }
+// The same copy addressed as a wave-uniform 64-bit base (SGPR pair) plus a
+// 32-bit per-lane byte offset: no per-lane 64-bit address arithmetic.
+__device__ __forceinline__ void copy16_to_lds(const void *sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds_addr)
+               : "memory", "m0");
+}
 
 // max / sum of a value with its partner lane in the other half of the wave.
 __device__ __forceinline__ float max_halves(float x) {
@@ -345,11 +353,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_bf16(const AttnArgs 
       voff[mb][s2] = C::TILE_BYTES +
                      C::off(4 * g + (i16 >> 2) + 8 * s2, 32 * mb + 16 * (G16 & 1) + 4 * (i16 & 3));
 
-  auto tile_at = [&](int ti, SegRange &sr, int &key0) {
-    sr = ti < nt0 ? sr0 : sr1;
-    key0 = sr.lo + (ti < nt0 ? ti : ti - nt0) * C::KT;
-  };
-
   // Copy cursor: tile cp_ti is copied next; cpk/cpv point at its first K/V
   // row and advance one tile per copy (switching segment once), so the
   // steady state needs no 64-bit address arithmetic.
@@ -362,40 +365,40 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_bf16(const AttnArgs 
     cpk = kseg1;
     cpv = vseg1;
   }
-  int cp_ti = 0;
+  bool cp_seg0 = nt0 > 0;               // cursor in the first segment
+  int cp_left = cp_seg0 ? nt0 : nt1;     // tiles left in the cursor's segment
+
+  // Whether copy u of this wave is a V block: a compile-time fact when the
+  // tile's blocks split evenly over the waves (K blocks first).
+  auto is_v = [&](int u) {
+    if constexpr (C::BLOCKS % NW == 0) return u >= C::CPW / 2;
+    else return ld_isv[u];
+  };
 
   // Copy the next tile (K and V) into LDS buffer `buf` and advance the
-  // cursor.  Rows past the valid range are clamped to the last valid row
-  // (finite data, masked in the softmax).
+  // cursor.  Only a segment's last tile can be ragged: its rows past the
+  // valid range are clamped to the last valid row (finite data, masked in
+  // the softmax).
   auto issue_next = [&](int buf) {
-    const bool partial = (cp_ti == nt0 - 1) || (cp_ti == ntiles - 1);
-    int nvalid = C::KT;
-    if (partial) {
-      SegRange sr;
-      int key0;
-      tile_at(cp_ti, sr, key0);
-      nvalid = sr.hi - key0;
-    }
-    if (nvalid >= C::KT) {
+    if (--cp_left != 0) {
 #pragma unroll
       for (int u = 0; u < C::CPW; ++u)
-        copy16_to_lds((const void *)((ld_isv[u] ? cpv : cpk) + ld_off[u]),
-                      (uint32_t)(uintptr_t)(bufp(buf) + ld_lds[u]));
+        copy16_to_lds(is_v(u) ? cpv : cpk, ld_off[u], (uint32_t)(uintptr_t)(bufp(buf) + ld_lds[u]));
+      cpk += kstep;
+      cpv += vstep;
     } else {
+      const SegRange &sr = cp_seg0 ? sr0 : sr1;
+      const int nvalid = (sr.hi - sr.lo) - ((cp_seg0 ? nt0 : nt1) - 1) * C::KT;
 #pragma unroll
       for (int u = 0; u < C::CPW; ++u) {
         const int row = min(ld_row[u], nvalid - 1);
-        const uint32_t o = (uint32_t)(row * (int)(ld_isv[u] ? a.v_ss : a.k_ss) + ld_col[u]) * 2u;
-        copy16_to_lds((const void *)((ld_isv[u] ? cpv : cpk) + o), (uint32_t)(uintptr_t)(bufp(buf) + ld_lds[u]));
+        const uint32_t o = (uint32_t)(row * (int)(is_v(u) ? a.v_ss : a.k_ss) + ld_col[u]) * 2u;
+        copy16_to_lds(is_v(u) ? cpv : cpk, o, (uint32_t)(uintptr_t)(bufp(buf) + ld_lds[u]));
       }
-    }
-    ++cp_ti;
-    if (cp_ti == nt0) {
       cpk = kseg1;
       cpv = vseg1;
-    } else {
-      cpk += kstep;
-      cpv += vstep;
+      cp_seg0 = false;
+      cp_left = nt1;
     }
   };
 
