@@ -790,52 +790,85 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Split-K reduction: fold the partials of each row in split order, then
-// write or merge the result.
+// Split-K reduction.  The nsplit partials of a row are softmax results over
+// disjoint key ranges; their combination is the log-sum-exp weighted mean
+//   lse = m + ln sum_s exp(lse_s - m),  out = sum_s exp(lse_s - lse) out_s
+// (m = max_s lse_s), the closed form of folding them with the merge rule.
+// One work-group per (batch, head, row): kSplitGroups groups of D/4 threads
+// (one float4 of the row each) take every kSplitGroups-th split, so each
+// thread issues few independent loads; the groups' sums meet in LDS.  Then
+// write, or merge into the running pair with the merge rule.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void split_reduce_kernel(const SplitArgs a) {
-  const int per_row = a.D / 4;
-  const int64_t f = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t total = (int64_t)a.B * a.H * a.rows * per_row;
-  if (f >= total) return;
-  const int d4 = (int)(f % per_row);
-  int64_t rest = f / per_row;
+constexpr int kSplitGroups = 8;
+
+template <int D>
+__global__ __launch_bounds__(kSplitGroups * D / 4) void split_reduce_kernel(const SplitArgs a) {
+  constexpr int per_row = D / 4;
+  __shared__ float s_max[kSplitGroups], s_wsum[kSplitGroups];
+  __shared__ f32x4 s_out[kSplitGroups][per_row];
+  const int d4 = threadIdx.x % per_row;
+  const int sg = threadIdx.x / per_row;
+  int64_t rest = blockIdx.x;
   const int tok = (int)(rest % a.rows);
   rest /= a.rows;
   const int h = (int)(rest % a.H);
   const int b = (int)(rest / a.H);
 
-  // Partials are folded in split order with the sigma rule; loads are issued
-  // eight splits at a time so the fold waits on few memory round trips.
-  constexpr int kChunk = 8;
-  f32x4 o = {0.f, 0.f, 0.f, 0.f};
-  float l = neg_inf();
   const int64_t split_stride = (int64_t)a.B * a.H * a.rows;
   const int64_t pr0 = ((int64_t)b * a.H + h) * a.rows + tok;
-  for (int s0 = 0; s0 < a.nsplit; s0 += kChunk) {
-    float bl[kChunk];
-    f32x4 bo[kChunk];
+  constexpr int kU = 4;  // splits per thread per round of loads
+  float m = neg_inf();
+  for (int s0 = sg; s0 < a.nsplit; s0 += kU * kSplitGroups) {
+    float lv[kU];
 #pragma unroll
-    for (int j = 0; j < kChunk; ++j) {
-      const int s = min(s0 + j, a.nsplit - 1);
-      const int64_t pr = pr0 + s * split_stride;
-      bl[j] = a.part_lse[pr];
-      bo[j] = *(const f32x4 *)(a.part_out + pr * a.D + 4 * d4);
-    }
+    for (int j = 0; j < kU; ++j) lv[j] = a.part_lse[pr0 + min(s0 + j * kSplitGroups, a.nsplit - 1) * split_stride];
 #pragma unroll
-    for (int j = 0; j < kChunk; ++j) {
-      if (s0 + j >= a.nsplit || bl[j] == neg_inf()) continue;
-      if (l == neg_inf()) {
-        o = bo[j];
-        l = bl[j];
-        continue;
+    for (int j = 0; j < kU; ++j) m = fmaxf(m, lv[j]);
+  }
+  if (d4 == 0) s_max[sg] = m;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kSplitGroups; ++j) m = fmaxf(m, s_max[j]);
+
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.0f;
+  if (m != neg_inf()) {
+    for (int s0 = sg; s0 < a.nsplit; s0 += kU * kSplitGroups) {
+      float lv[kU];
+      f32x4 po[kU];
+#pragma unroll
+      for (int j = 0; j < kU; ++j) {
+        const int64_t pr = pr0 + min(s0 + j * kSplitGroups, a.nsplit - 1) * split_stride;
+        lv[j] = a.part_lse[pr];
+        po[j] = *(const f32x4 *)(a.part_out + pr * D + 4 * d4);
       }
-      const float diff = bl[j] - l;
-      const float w = 1.0f / (1.0f + __expf(-diff));
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = o[e] - w * (o[e] - bo[j][e]);
-      l = fmaxf(l, bl[j]) + log1pf(__expf(-fabsf(diff)));
+      for (int j = 0; j < kU; ++j) {
+        const float w = (s0 + j * kSplitGroups < a.nsplit) ? __expf(lv[j] - m) : 0.0f;  // 0 for an empty split
+        wsum += w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = __builtin_fmaf(w, po[j][e], o[e]);
+      }
     }
+  }
+  s_out[sg][d4] = o;
+  if (d4 == 0) s_wsum[sg] = wsum;
+  __syncthreads();
+  if (sg != 0) return;
+  float l = neg_inf();
+  if (m != neg_inf()) {
+    wsum = 0.0f;
+    o = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < kSplitGroups; ++j) {
+      wsum += s_wsum[j];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] += s_out[j][d4][e];
+    }
+    const float inv = 1.0f / wsum;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] *= inv;
+    l = m + __logf(wsum);
   }
 
   const int orow = a.o_row0 + tok;
@@ -914,10 +947,13 @@ int launch_merge(const MergeArgs &a, void *stream) {
 }
 
 int launch_split_reduce(const SplitArgs &a, void *stream) {
-  const int64_t total = (int64_t)a.B * a.H * a.rows * (a.D / 4);
-  if (total == 0) return 0;
-  const dim3 grid((unsigned)((total + 255) / 256)), block(256);
-  hipLaunchKernelGGL(split_reduce_kernel, grid, block, 0, (hipStream_t)stream, a);
+  const int64_t rows = (int64_t)a.B * a.H * a.rows;
+  if (rows == 0) return 0;
+  const dim3 grid((unsigned)rows);
+  if (a.D == 128)
+    split_reduce_kernel<128><<<grid, dim3(kSplitGroups * 32), 0, (hipStream_t)stream>>>(a);
+  else
+    split_reduce_kernel<64><<<grid, dim3(kSplitGroups * 16), 0, (hipStream_t)stream>>>(a);
   return (int)hipGetLastError();
 }
 
