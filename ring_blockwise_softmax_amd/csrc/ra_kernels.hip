@@ -59,19 +59,16 @@ __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 // memory clobber keeps the compiler from moving accesses across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-// 16 bytes per lane from global memory straight into LDS: lane i's bytes land
+// 16 bytes per lane from global memory straight into LDS: lane i reads
+// sbase + voff (a wave-uniform 64-bit base in an SGPR pair plus a 32-bit
+// lane offset, so no per-lane 64-bit address arithmetic) and its bytes land
 // at lds_addr + 16*i.  Written as inline asm so that the compiler does not
 // track these copies and wait for them before unrelated LDS reads; the
 // kernels wait for them explicitly (s_waitcnt vmcnt) before publishing a
-// tile.  No register outputs; the address is consumed at issue.
-__device__ __forceinline__ void copy16_to_lds(const void *g, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(g), "s"(lds_addr)
-               : "memory", "m0");
-}
-// The same copy addressed as a wave-uniform 64-bit base (SGPR pair) plus a
-// 32-bit per-lane byte offset: no per-lane 64-bit address arithmetic.
+// tile.  No register outputs; the addresses are consumed at issue.  The LDS
+// destination is taken from M0, which the asm sets (one wait state before
+// the copy reads it) and declares clobbered; nothing else in these kernels
+// keeps a value in M0 (gfx950 LDS instructions do not use it).
 __device__ __forceinline__ void copy16_to_lds(const void *sbase, uint32_t voff, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
