@@ -105,7 +105,8 @@ __device__ __forceinline__ bool decode_tile(const AttnArgs &a, Tile &t) {
   while (it + 1 < a.nitems && tt >= a.items[it + 1].tile0) ++it;
   t.item = it;
   const int e = tt - a.items[it].tile0;
-  t.qt = e / a.items[it].nsplit;
+  // last query tile first: under a causal mask it sees the most keys
+  t.qt = a.items[it].nqt - 1 - e / a.items[it].nsplit;
   t.split = e % a.items[it].nsplit;
   return true;
 }
