@@ -221,10 +221,11 @@ __device__ __forceinline__ void epilogue(const AttnArgs &a, const KItem &it, con
 // (QT = 32*NW).  Keys advance in 32-key tiles held in a ring of four LDS
 // buffers (K and V each).  Tiles are copied straight from global memory into
 // LDS with global_load_lds_dwordx4 (no staging registers), three tiles ahead
-// of use, with one barrier per tile.  The four buffers are distinct LDS
-// objects: that lets the compiler see that reads of one buffer do not alias
-// the copies in flight into another, so it does not wait for those copies.
-// The loop is software-pipelined by one tile: while the VALUs turn S(j) into
+// of use, with one barrier per tile.  The copies are inline asm, invisible
+// to the compiler's wait insertion, so LDS reads of one buffer never wait
+// for copies in flight into another; each stage waits for its own tile
+// (s_waitcnt vmcnt) before the barrier that publishes it.  The loop is
+// software-pipelined by one tile: while the VALUs turn S(j) into
 // probabilities, the matrix cores already compute S(j+1) = K(j+1) Q^T.
 //
 // LDS rows are unpadded (2*D bytes) with the 16-byte chunks of each row
