@@ -746,7 +746,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_f32(const AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Standalone merge: one float4 of one (row, head) per thread.
+// Standalone merge: one float4 of one (row, head) per thread.  Both outputs
+// and the partial are streamed once, so the float4 traffic is non-temporal.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
   const int per_row = a.D / 4;
@@ -775,7 +776,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
   const float blse = *blp;
   const float lse = *lp;
   const f32x4 bo = __builtin_nontemporal_load((const f32x4 *)bop);
-  const f32x4 o = *(const f32x4 *)op;
+  const f32x4 o = __builtin_nontemporal_load((const f32x4 *)op);
   const bool block_empty = blse == neg_inf();
   const bool run_empty = lse == neg_inf();
   const float diff = blse - lse;  // used only when both are finite
@@ -783,7 +784,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
   f32x4 r;
 #pragma unroll
   for (int j = 0; j < 4; ++j) r[j] = block_empty ? o[j] : (run_empty ? bo[j] : o[j] - w * (o[j] - bo[j]));
-  *(f32x4 *)op = r;
+  __builtin_nontemporal_store(r, (f32x4 *)op);
   if (d4 == 0)
     *lp = block_empty ? lse : (run_empty ? blse : fmaxf(lse, blse) + log1pf(__expf(-fabsf(diff))));
 }
