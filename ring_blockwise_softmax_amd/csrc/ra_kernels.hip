@@ -754,12 +754,23 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
   const int64_t f = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t total = (int64_t)a.B * a.total_rows * a.H * per_row;
   if (f >= total) return;
-  const int d4 = (int)(f % per_row);
-  int64_t rest = f / per_row;
-  const int h = (int)(rest % a.H);
-  rest /= a.H;
-  const int row = (int)(rest % a.total_rows);
-  const int b = (int)(rest / a.total_rows);
+  int d4, h, row, b;
+  if (total < ((int64_t)1 << 31)) {  // 32-bit index arithmetic
+    const uint32_t f32 = (uint32_t)f;
+    d4 = (int)(f32 % (uint32_t)per_row);
+    uint32_t rest = f32 / (uint32_t)per_row;
+    h = (int)(rest % (uint32_t)a.H);
+    rest /= (uint32_t)a.H;
+    row = (int)(rest % (uint32_t)a.total_rows);
+    b = (int)(rest / (uint32_t)a.total_rows);
+  } else {
+    d4 = (int)(f % per_row);
+    int64_t rest = f / per_row;
+    h = (int)(rest % a.H);
+    rest /= a.H;
+    row = (int)(rest % a.total_rows);
+    b = (int)(rest / a.total_rows);
+  }
   int k = 0;
   while (k + 1 < a.nranges && row >= a.ranges[k + 1].prefix) ++k;
   const int off = row - a.ranges[k].prefix;
