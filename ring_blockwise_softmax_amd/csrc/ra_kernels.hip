@@ -69,11 +69,18 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "me
 // destination is taken from M0, which the asm sets (one wait state before
 // the copy reads it) and declares clobbered; nothing else in these kernels
 // keeps a value in M0 (gfx950 LDS instructions do not use it).
+template <bool NT>
 __device__ __forceinline__ void copy16_to_lds(const void *sbase, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(sbase), "s"(lds_addr)
-               : "memory", "m0");
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(lds_addr)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(lds_addr)
+                 : "memory", "m0");
 }
 
 // max / sum of a value with its partner lane in the other half of the wave.
@@ -261,8 +268,10 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 
-// Two waves per SIMD: 8 / NW work-groups per CU.
-template <int D, int NW, int NBUF>
+// Two waves per SIMD: 8 / NW work-groups per CU.  NT: K/V are streamed once
+// (no other work-group reads them), so their copies carry the non-temporal
+// hint.
+template <int D, int NW, int NBUF, bool NT>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_bf16(const AttnArgs a) {
   using C = Bf16Cfg<D, NW, NBUF>;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[];
@@ -382,7 +391,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_bf16(const AttnArgs 
     if (--cp_left != 0) {
 #pragma unroll
       for (int u = 0; u < C::CPW; ++u)
-        copy16_to_lds(is_v(u) ? cpv : cpk, ld_off[u], (uint32_t)(uintptr_t)(bufp(buf) + ld_lds[u]));
+        copy16_to_lds<NT>(is_v(u) ? cpv : cpk, ld_off[u], (uint32_t)(uintptr_t)(bufp(buf) + ld_lds[u]));
       cpk += kstep;
       cpv += vstep;
     } else {
@@ -392,7 +401,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_bf16(const AttnArgs 
       for (int u = 0; u < C::CPW; ++u) {
         const int row = min(ld_row[u], nvalid - 1);
         const uint32_t o = (uint32_t)(row * (int)(is_v(u) ? a.v_ss : a.k_ss) + ld_col[u]) * 2u;
-        copy16_to_lds(is_v(u) ? cpv : cpk, o, (uint32_t)(uintptr_t)(bufp(buf) + ld_lds[u]));
+        copy16_to_lds<NT>(is_v(u) ? cpv : cpk, o, (uint32_t)(uintptr_t)(bufp(buf) + ld_lds[u]));
       }
       cpk = kseg1;
       cpv = vseg1;
@@ -915,12 +924,12 @@ static int set_lds(K kernel, size_t bytes, bool &done) {
   return 0;
 }
 
-template <int D, int NW, int NBUF>
+template <int D, int NW, int NBUF, bool NT>
 static int launch_bf16(const AttnArgs &a, dim3 grid, hipStream_t s) {
   static bool done = false;
-  const int rc = set_lds(attn_fwd_bf16<D, NW, NBUF>, Bf16Cfg<D, NW, NBUF>::LDS_BYTES, done);
+  const int rc = set_lds(attn_fwd_bf16<D, NW, NBUF, NT>, Bf16Cfg<D, NW, NBUF>::LDS_BYTES, done);
   if (rc) return rc;
-  attn_fwd_bf16<D, NW, NBUF><<<grid, dim3(64 * NW), Bf16Cfg<D, NW, NBUF>::LDS_BYTES, s>>>(a);
+  attn_fwd_bf16<D, NW, NBUF, NT><<<grid, dim3(64 * NW), Bf16Cfg<D, NW, NBUF>::LDS_BYTES, s>>>(a);
   return 0;
 }
 
@@ -938,10 +947,16 @@ int launch_attn(const AttnArgs &a, int dtype, int head_dim, int nw, void *stream
   hipStream_t s = (hipStream_t)stream;
   int rc;
   if (dtype == 0) {
+    // K/V read by exactly one work-group (one query tile per item, all the
+    // query heads of a K/V head packed into it, e.g. decode): stream them.
+    bool streamed = a.GP == a.G;
+    for (int i = 0; i < a.nitems; ++i) streamed = streamed && a.items[i].nqt == 1;
     if (nw == 8)
-      rc = head_dim == 128 ? launch_bf16<128, 8, 4>(a, grid, s) : launch_bf16<64, 8, 4>(a, grid, s);
+      rc = head_dim == 128 ? launch_bf16<128, 8, 4, false>(a, grid, s) : launch_bf16<64, 8, 4, false>(a, grid, s);
+    else if (streamed)
+      rc = head_dim == 128 ? launch_bf16<128, 4, 4, true>(a, grid, s) : launch_bf16<64, 4, 4, true>(a, grid, s);
     else
-      rc = head_dim == 128 ? launch_bf16<128, 4, 4>(a, grid, s) : launch_bf16<64, 4, 4>(a, grid, s);
+      rc = head_dim == 128 ? launch_bf16<128, 4, 4, false>(a, grid, s) : launch_bf16<64, 4, 4, false>(a, grid, s);
   } else {
     rc = head_dim == 128 ? launch_f32<128>(a, grid, block, s) : launch_f32<64>(a, grid, block, s);
   }
