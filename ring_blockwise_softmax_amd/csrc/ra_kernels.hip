@@ -9,7 +9,8 @@
 //     lse <- lse - ln sigmoid(lse - blse)
 // evaluated in its overflow-free form max(lse, blse) + log1p(exp(-|diff|)).
 //
-// Kernel shape (bf16 path, one work-group = 4 waves = 128 packed query rows):
+// Kernel shape (bf16 path; one work-group = 4 waves = 128 packed query rows,
+// or 8 waves = 256 as a tuning option):
 //  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //    the key index runs down the MFMA M dimension and the query index across
 //    N, so each lane owns one query column and the softmax row reductions are
@@ -18,8 +19,9 @@
 //    registers are already laid out as the B operand, so P never touches LDS.
 //    The V^T A operand comes from the row-major V tile through
 //    ds_read_b64_tr_b16 (16-lane transpose reads), so V is staged as loaded.
-//  * K/V tiles of 64 keys are double-buffered in LDS; the next tile's global
-//    loads are in flight while the current one is consumed (one barrier/tile).
+//  * K/V tiles of 32 keys go global -> LDS directly (global_load_lds_dwordx4)
+//    into a 4-deep ring, three tiles ahead of use, one barrier per tile; the
+//    S products of tile j+1 are issued while the softmax of tile j runs.
 //  * Online softmax in the exp2 domain with a lazy rescale: the running
 //    maximum used for exponentiation only moves when a row's maximum grows
 //    by more than 2^8, so the accumulator is rarely rescaled; the final
@@ -27,8 +29,8 @@
 //  * Work tiles are assigned XCD-contiguously: consecutive tiles of one
 //    (batch, head) land on the same XCD and share its L2 copy of K/V.
 //
-// The fp32 path has the same structure on v_mfma_f32_32x32x2_f32, with no
-// rounding of inputs or probabilities anywhere.
+// The fp32 path computes the same thing on v_mfma_f32_32x32x2_f32 with K/V
+// staged through registers, with no rounding of inputs or probabilities.
 
 #include <hip/hip_runtime.h>
 
@@ -361,9 +363,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_bf16(const AttnArgs 
       voff[mb][s2] = C::TILE_BYTES +
                      C::off(4 * g + (i16 >> 2) + 8 * s2, 32 * mb + 16 * (G16 & 1) + 4 * (i16 & 3));
 
-  // Copy cursor: tile cp_ti is copied next; cpk/cpv point at its first K/V
-  // row and advance one tile per copy (switching segment once), so the
-  // steady state needs no 64-bit address arithmetic.
+  // Copy cursor: cpk/cpv point at the first K/V row of the next tile to copy
+  // and advance one tile per copy (switching segment once), so the steady
+  // state needs no 64-bit address arithmetic.
   const int64_t kstep = (int64_t)C::KT * a.k_ss * 2, vstep = (int64_t)C::KT * a.v_ss * 2;
   const char *kseg1 = reinterpret_cast<const char *>(kbase + (int64_t)(sr1.kv_start + sr1.lo) * a.k_ss);
   const char *vseg1 = reinterpret_cast<const char *>(vbase + (int64_t)(sr1.kv_start + sr1.lo) * a.v_ss);
@@ -496,8 +498,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_bf16(const AttnArgs 
   f32x16 s_a = f32x16{}, s_b = f32x16{};
   // Tiles are copied PF = NBUF-1 tiles ahead of use.  Copies complete in
   // order, so "tile j+1 has landed" is "at most (copies issued after it) are
-  // still outstanding": wait_vm(n) waits until at most n copy instructions
-  // per wave remain.
+  // still outstanding": wait_vm(t) waits until at most the copies of t tiles
+  // (t * CPW instructions per wave) remain.
   constexpr int PF = NBUF - 1;
   auto wait_vm = [&](int tiles_after) {
     // at most n = tiles_after * CPW copies may remain; s_waitcnt takes an
