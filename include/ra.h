@@ -38,7 +38,8 @@
  *  - bf16 inputs are multiplied on the matrix cores with fp32 accumulation;
  *    the softmax probabilities are rounded to bf16 (round to nearest even)
  *    before the P*V product.  fp32 inputs are computed in fp32 throughout.
- *  - Supported head_dim: 64 and 128.  Sizes up to 2^31-1 tokens per sequence.
+ *  - Supported head_dim: 64 and 128.  Sizes up to 2^31-1 tokens per sequence;
+ *    head strides (sh) up to 2^31-1 elements.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Every call is
  *    asynchronous on that stream; device faults surface at the caller's next
  *    synchronisation.

@@ -47,6 +47,7 @@ ra_status check_tensor(const ra_tensor *t, const char *name, bool is_lse) {
   if (t->s > INT32_MAX - 1 || t->b > INT32_MAX || t->h > 65535)
     return fail(RA_E_UNSUPPORTED, "%s: sizes beyond the supported range", name);
   if (t->sb < 0 || t->ss < 0 || t->sh < 0) return fail(RA_E_INVALID, "%s: negative stride", name);
+  if (t->sh > INT32_MAX) return fail(RA_E_UNSUPPORTED, "%s: head stride beyond 2^31-1 elements", name);
   const bool nonempty = t->b > 0 && t->s > 0;
   if (nonempty && !t->data) return fail(RA_E_INVALID, "%s: null data pointer", name);
   if (is_lse) {

@@ -79,6 +79,7 @@ def test_status_strings():
     (lambda a: a[4].__setattr__("data", FAKE + 2), RA_E_ALIGN),         # lse alignment
     (lambda a: a[2].__setattr__("s", 32), RA_E_INVALID),                 # k/v length differ
     (lambda a: a[1].__setattr__("b", 2), RA_E_INVALID),                  # batch mismatch
+    (lambda a: a[0].__setattr__("sh", 1 << 33), RA_E_UNSUPPORTED),        # head stride > int32
 ])
 def test_block_attn_rejects(mutate, status):
     args = list(good())
