@@ -190,7 +190,14 @@ void finish_tiles(AttnArgs &a, int QT) {
   a.ntiles = tile;
   const int64_t nw = (int64_t)a.B * a.nhb * a.ntiles;
   a.n_work = (int32_t)nw;
-  a.per_xcd = (int32_t)((nw + 7) / 8);
+  const int64_t pairs = (int64_t)a.B * a.nhb;
+  if (pairs % 8 == 0) {  // whole (batch, head block) pairs per XCD
+    a.per_xcd_pairs = (int32_t)(pairs / 8);
+    a.per_xcd = a.per_xcd_pairs * a.ntiles;
+  } else {  // consecutive work indices split over the XCDs
+    a.per_xcd_pairs = 0;
+    a.per_xcd = (int32_t)((nw + 7) / 8);
+  }
 }
 
 KItem to_kitem(const ra_plan_item &p, int64_t o_row0) {

@@ -52,12 +52,12 @@ struct AttnArgs {
   int32_t nhb;                    // head blocks = Hq / GP
   int32_t ntiles;                 // work tiles per (batch, head block)
   int32_t n_work;                 // B * nhb * ntiles
-  int32_t per_xcd;                // ceil(n_work / 8): XCD-contiguous work ranges
+  int32_t per_xcd;                // work-groups per XCD (grid = 8 * per_xcd)
+  int32_t per_xcd_pairs;          // B * nhb / 8 when that divides evenly, else 0
   int32_t mode;                   // OutMode
   int32_t part_rows;              // rows per split in the partial buffers (q_len of item 0)
   int32_t nitems;
   float scale_log2;               // softmax scale * log2(e)
-  float pad0;
   KItem items[kMaxItems];
 };
 

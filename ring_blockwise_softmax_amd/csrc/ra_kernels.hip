@@ -103,20 +103,45 @@ struct Tile {
 };
 
 __device__ __forceinline__ bool decode_tile(const AttnArgs &a, Tile &t) {
+  // When the (batch, head block) pairs divide evenly over the 8 XCDs they
+  // are cut into 8 contiguous chunks, one per XCD (blockIdx % 8), so every
+  // XCD gets the same mix of items and its L2 holds the K/V of its own heads.  Within an XCD the order is item-major
+  // (items come heaviest first), then pair, then query tile (last tile first:
+  // under a causal mask it sees the most keys) and split.
   const int L = blockIdx.x;
-  const int idx = (L & 7) * a.per_xcd + (L >> 3);
-  if (idx >= a.n_work) return false;
-  const int tt = idx % a.ntiles;
-  const int rest = idx / a.ntiles;
-  t.hb = rest % a.nhb;
-  t.b = rest / a.nhb;
+  const int x = L & 7, l = L >> 3;
+  if (a.per_xcd_pairs == 0) {
+    // fewer pairs than XCDs (or not a multiple of 8): consecutive work
+    // indices, head-major, split evenly over the XCDs
+    const int idx = x * a.per_xcd + l;
+    if (idx >= a.n_work) return false;
+    const int tt = idx % a.ntiles;
+    const int rest = idx / a.ntiles;
+    t.hb = rest % a.nhb;
+    t.b = rest / a.nhb;
+    int it = 0;
+    while (it + 1 < a.nitems && tt >= a.items[it + 1].tile0) ++it;
+    t.item = it;
+    const int e = tt - a.items[it].tile0;
+    t.qt = a.items[it].nqt - 1 - e / a.items[it].nsplit;
+    t.split = e % a.items[it].nsplit;
+    return true;
+  }
+  const int np = a.per_xcd_pairs;
+  const int p0 = x * np;
+  if (l >= np * a.ntiles) return false;
   int it = 0;
-  while (it + 1 < a.nitems && tt >= a.items[it + 1].tile0) ++it;
+  while (it + 1 < a.nitems && l >= np * a.items[it + 1].tile0) ++it;
   t.item = it;
-  const int e = tt - a.items[it].tile0;
-  // last query tile first: under a causal mask it sees the most keys
-  t.qt = a.items[it].nqt - 1 - e / a.items[it].nsplit;
-  t.split = e % a.items[it].nsplit;
+  const KItem &item = a.items[it];
+  const int per_pair = item.nqt * item.nsplit;
+  const int e = l - np * item.tile0;
+  const int pair = p0 + e / per_pair;
+  const int tt = e % per_pair;
+  t.hb = pair % a.nhb;
+  t.b = pair / a.nhb;
+  t.qt = item.nqt - 1 - tt / item.nsplit;
+  t.split = tt % item.nsplit;
   return true;
 }
 
