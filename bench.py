@@ -180,7 +180,38 @@ def merge_bench(steps=10):
         "peak_GBs": PEAK_HBM_GBS,
         "frac": nbytes / per / 1e6 / PEAK_HBM_GBS,
         "copy_GBs": nbytes / copy_ms / 1e6,
+        "step_shape": merge_step_bench(),
     }
+
+
+def merge_step_bench(steps=12, sets=4):
+    """Standalone merge at the 24k MHA step shape (all ranks' rows of one
+    ring step: 1.19 GB, 297 MB per rank), cycling through `sets` buffer sets
+    so that one call's operands are not still cached from the previous call."""
+    import torch
+
+    import ring_blockwise_softmax_amd as ra
+
+    B, S, H, D = 1, 24000, 32, 128
+    g = torch.Generator(device="cuda").manual_seed(45)
+    bufs = [(torch.randn(B, S, H, D, device="cuda", generator=g), torch.randn(B, H, S, device="cuda", generator=g),
+             torch.randn(B, S, H, D, device="cuda", generator=g), torch.randn(B, H, S, device="cuda", generator=g))
+            for _ in range(sets)]
+    for i in range(sets):
+        ra.merge(*bufs[i])
+    torch.cuda.synchronize()
+    ra.profile_enable(True)
+    for i in range(steps):
+        ra.merge(*bufs[i % sets])
+    prof = ra.profile_read()
+    ra.profile_enable(False)
+    n, ms = prof["merge"]
+    per = ms / n
+    nbytes = B * S * H * (3 * 4 * D + 12)
+    del bufs
+    torch.cuda.empty_cache()
+    return {"shape": f"B{B} S{S} H{H} d{D} fp32, {sets} rotating buffer sets", "bytes": nbytes, "ms": per,
+            "achieved_GBs": nbytes / per / 1e6, "frac": nbytes / per / 1e6 / PEAK_HBM_GBS}
 
 
 def main():
