@@ -131,26 +131,13 @@ struct ProfScope {
 // Work tables
 // ---------------------------------------------------------------------------
 struct Geometry {
-  int QT, KT, nw;
+  int QT, KT;
 };
 
-// Waves per work-group of the bf16 kernel (32 query rows each).
-// RA_BF16_WAVES (4 or 8) overrides the default; used for tuning sweeps only.
-int bf16_waves() {
-  static int nw = [] {
-    const char *e = getenv("RA_BF16_WAVES");
-    const int v = e ? atoi(e) : 4;
-    return (v == 8) ? 8 : 4;
-  }();
-  return nw;
-}
-
 // Tile geometry of the attention kernel for a dtype.
-Geometry geometry(int dtype, int64_t rows = 0) {
-  (void)rows;
-  if (dtype != RA_BF16) return Geometry{kQTileF32, kKTileF32, 4};
-  const int nw = bf16_waves();
-  return Geometry{32 * nw, kKTileBF16, nw};
+Geometry geometry(int dtype) {
+  if (dtype != RA_BF16) return Geometry{kQTileF32, kKTileF32};
+  return Geometry{kQTileBF16, kKTileBF16};
 }
 
 void fill_strides(AttnArgs &a, const ra_tensor *q, const ra_tensor *k, const ra_tensor *v) {
@@ -252,7 +239,7 @@ size_t split_bytes(const Split &s, int64_t B, int64_t H, int64_t rows, int64_t D
 // written (mode kWrite) or merged (kMerge) into the destination held in `a`.
 ra_status run_single_item(AttnArgs a, int dtype, int D, char *ws, size_t ws_bytes, void *stream) {
   KItem &it = a.items[0];
-  const Geometry geo = geometry(dtype, (int64_t)it.q_len * a.GP);
+  const Geometry geo = geometry(dtype);
   const int64_t nqt = (int64_t(it.q_len) * a.GP + geo.QT - 1) / geo.QT;
   const int64_t wgs = (int64_t)a.B * (a.Hq / a.GP) * nqt;
   Split sp = (it.nseg == 1) ? choose_split(wgs, it.seg[0].kv_len, geo.KT) : Split{};
@@ -262,7 +249,7 @@ ra_status run_single_item(AttnArgs a, int dtype, int D, char *ws, size_t ws_byte
     finish_tiles(a, geo.QT);
     if (a.n_work == 0) return RA_OK;
     ProfScope ps(RA_KERNEL_ATTN, stream);
-    const int rc = launch_attn(a, dtype, D, geo.nw, stream);
+    const int rc = launch_attn(a, dtype, D, stream);
     return rc ? hip_fail(rc, "attention launch") : RA_OK;
   }
   it.nsplit = sp.nsplit;
@@ -283,7 +270,7 @@ ra_status run_single_item(AttnArgs a, int dtype, int D, char *ws, size_t ws_byte
   finish_tiles(a, geo.QT);
   {
     ProfScope ps(RA_KERNEL_ATTN, stream);
-    const int rc = launch_attn(a, dtype, D, geo.nw, stream);
+    const int rc = launch_attn(a, dtype, D, stream);
     if (rc) return hip_fail(rc, "attention launch");
   }
   ProfScope ps(RA_KERNEL_SPLIT_REDUCE, stream);
@@ -292,7 +279,7 @@ ra_status run_single_item(AttnArgs a, int dtype, int D, char *ws, size_t ws_byte
 }
 
 size_t single_item_ws(int dtype, int64_t B, int64_t Hq, int GP, int64_t q_len, int64_t kv_len, int64_t D) {
-  const Geometry geo = geometry(dtype, q_len * GP);
+  const Geometry geo = geometry(dtype);
   const int64_t nqt = (q_len * GP + geo.QT - 1) / geo.QT;
   const int64_t wgs = B * (Hq / GP) * nqt;
   return split_bytes(choose_split(wgs, kv_len, geo.KT), B, Hq, q_len, D);
@@ -484,7 +471,7 @@ ra_status ra_ring_forward(const ra_tensor *q, const ra_tensor *k, const ra_tenso
   int64_t qlen_max = 0;
   for (auto &p : rs.items) qlen_max = std::max(qlen_max, p.q_len);
   base.GP = choose_gp(qlen_max, base.G, geometry(dtype).QT);
-  const Geometry geo = geometry(dtype, qlen_max * base.GP);
+  const Geometry geo = geometry(dtype);
 
   for (int t = 0; t < P; ++t) {
     std::vector<ra_plan_item> step;
@@ -532,7 +519,7 @@ ra_status ra_ring_forward(const ra_tensor *q, const ra_tensor *k, const ra_tenso
         finish_tiles(a, geo.QT);
         if (a.n_work > 0) {
           ProfScope ps(RA_KERNEL_ATTN, stream);
-          const int rc = launch_attn(a, dtype, D, geo.nw, stream);
+          const int rc = launch_attn(a, dtype, D, stream);
           if (rc) return hip_fail(rc, "attention launch");
         }
       }

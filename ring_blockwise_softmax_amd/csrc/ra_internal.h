@@ -93,12 +93,13 @@ struct SplitArgs {
 };
 
 // Launchers (defined in ra_kernels.hip).  Return a hipError_t as int.
-int launch_attn(const AttnArgs &a, int dtype, int head_dim, int nw, void *stream);
+int launch_attn(const AttnArgs &a, int dtype, int head_dim, void *stream);
 int launch_merge(const MergeArgs &a, void *stream);
 int launch_split_reduce(const SplitArgs &a, void *stream);
 
 // Tile geometry the host needs for planning.
 constexpr int kQTileF32 = 128;   // packed query rows per work-group (fp32 kernel)
+constexpr int kQTileBF16 = 128;  // packed query rows per work-group (bf16 kernel: 4 waves x 32)
 constexpr int kKTileBF16 = 32;   // keys per LDS tile (bf16)
 constexpr int kKTileF32 = 32;    // keys per LDS tile (fp32)
 

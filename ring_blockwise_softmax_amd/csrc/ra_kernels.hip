@@ -251,28 +251,34 @@ __device__ __forceinline__ void epilogue(const AttnArgs &a, const KItem &it, con
 // ---------------------------------------------------------------------------
 // bf16 kernel
 // ---------------------------------------------------------------------------
-// One work-group = NW waves (4 or 8), each owning 32 packed query rows
-// (QT = 32*NW).  Keys advance in 32-key tiles held in a ring of four LDS
-// buffers (K and V each).  Tiles are copied straight from global memory into
-// LDS with global_load_lds_dwordx4 (no staging registers), three tiles ahead
-// of use, with one barrier per tile.  The copies are inline asm, invisible
-// to the compiler's wait insertion, so LDS reads of one buffer never wait
-// for copies in flight into another; each stage waits for its own tile
-// (s_waitcnt vmcnt) before the barrier that publishes it.  The loop is
-// software-pipelined by one tile: while the VALUs turn S(j) into
-// probabilities, the matrix cores already compute S(j+1) = K(j+1) Q^T.
+// One work-group = 4 waves, each owning 32 packed query rows (QT = 128).
+// Keys advance in 32-key tiles held in a ring of three LDS buffers (K then V
+// in each).  Tiles are copied straight from global memory into LDS with
+// global_load_lds_dwordx4 (no staging registers), two tiles ahead of use,
+// with one barrier per tile.  The copies are inline asm, invisible to the
+// compiler's wait insertion, so LDS reads of one buffer never wait for
+// copies in flight into another; each stage waits for its own tile
+// (s_waitcnt vmcnt) before the barrier that publishes it.
+//
+// There is no software pipeline inside a wave: a stage computes S, the
+// softmax and P*V of its tile in order.  Instead the kernel is sized for
+// three work-groups per CU (<= 168 VGPRs, 48 KB LDS each for d = 128), so
+// each SIMD runs three waves of three independent work-groups whose phases
+// drift apart: one wave's exponentials overlap another's matrix products.
 //
 // LDS rows are unpadded (2*D bytes) with the 16-byte chunks of each row
 // permuted by an XOR swizzle, chosen so that both the K operand reads (16
 // rows x 16 B per group of 16 lanes) and the V transpose reads (4 rows x
 // 64 B per half-wave) hit 64 distinct banks.
-template <int D, int NW_, int NBUF_>
+template <int D>
 struct Bf16Cfg {
-  static constexpr int NW = NW_;                      // waves per work-group
+  static constexpr int NW = 4;                        // waves per work-group
   static constexpr int THREADS = 64 * NW;
   static constexpr int KT = kKTileBF16;               // keys per LDS tile (32)
   static constexpr int QT = 32 * NW;                  // packed rows per work-group
-  static constexpr int NBUF = NBUF_;                  // ring of LDS buffers (even)
+  static constexpr int NBUF = 3;                      // ring of LDS buffers
+  static constexpr int PF = NBUF - 1;                 // tiles copied ahead of use
+  static constexpr int OCC = D == 128 ? 3 : 4;        // work-groups per CU
   static constexpr int ROWB = 2 * D;                  // bytes per LDS row
   static constexpr int TILE_BYTES = KT * ROWB;        // one tensor, one tile
   static constexpr int BUF_BYTES = 2 * TILE_BYTES;    // K then V
@@ -281,8 +287,8 @@ struct Bf16Cfg {
   static constexpr int CPW = 2 * BLOCKS / NW;         // blocks (K and V) copied per wave
   static constexpr int RPB = 1024 / ROWB;             // rows per block
   static constexpr int CH = D / 8;                    // 16-byte chunks per row
-  static_assert(CPW >= 1 && (2 * BLOCKS) % NW == 0, "tile blocks must split evenly over the waves");
-  static_assert(NBUF >= 4 && NBUF % 2 == 0, "the unrolled loop alternates two score registers");
+  static_assert(BLOCKS % NW == 0, "K and V blocks must split evenly over the waves");
+  static_assert(OCC * LDS_BYTES <= 160 * 1024, "LDS of the resident work-groups");
   __device__ static int swz(int r) {
     if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
     else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
@@ -295,12 +301,11 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 
-// Two waves per SIMD: 8 / NW work-groups per CU.  NT: K/V are streamed once
-// (no other work-group reads them), so their copies carry the non-temporal
-// hint.
-template <int D, int NW, int NBUF, bool NT>
-__global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_bf16(const AttnArgs a) {
-  using C = Bf16Cfg<D, NW, NBUF>;
+// NT: K/V are streamed once (no other work-group reads them), so their
+// copies carry the non-temporal hint.
+template <int D, bool NT>
+__global__ __launch_bounds__(Bf16Cfg<D>::THREADS, Bf16Cfg<D>::OCC) void attn_fwd_bf16(const AttnArgs a) {
+  using C = Bf16Cfg<D>;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[];
   // Buffer b of the ring (b is a compile-time constant after unrolling).
   auto bufp = [&](int b) -> lds_u8 * { return (lds_u8 *)smem_raw + b * C::BUF_BYTES; };
@@ -358,22 +363,20 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_bf16(const AttnArgs 
   const bf16 *vbase = reinterpret_cast<const bf16 *>(a.v) + (int64_t)t.b * a.v_sb + (int64_t)hkv * a.v_sh;
 
   // Direct-load geometry: this wave copies blocks bi = wave + NW*u of the
-  // tile (K blocks first, then V).  Block b covers tile rows b*RPB ..; lane
-  // writes physical chunk lane%CH of row b*RPB + lane/CH, which holds logical
-  // chunk (lane%CH) ^ swz(row).  Byte offsets are from the tile's first row,
-  // for full tiles (clamped rows are recomputed on partial ones).
+  // tile (K blocks for u < CPW/2, then V).  Block b covers tile rows b*RPB ..;
+  // lane writes physical chunk lane%CH of row b*RPB + lane/CH, which holds
+  // logical chunk (lane%CH) ^ swz(row).  Byte offsets are from the tile's
+  // first row, for full tiles (clamped rows are recomputed on partial ones).
+  auto is_v = [](int u) { return u >= C::CPW / 2; };
   int ld_row[C::CPW], ld_col[C::CPW], ld_lds[C::CPW];
   uint32_t ld_off[C::CPW];
-  bool ld_isv[C::CPW];
 #pragma unroll
   for (int u = 0; u < C::CPW; ++u) {
-    const int bi = wave + C::NW * u;
-    ld_isv[u] = bi >= C::BLOCKS;
-    const int blk = ld_isv[u] ? bi - C::BLOCKS : bi;
+    const int blk = wave + C::NW * (is_v(u) ? u - C::CPW / 2 : u);
     ld_row[u] = blk * C::RPB + lane / C::CH;
     ld_col[u] = (((lane % C::CH) ^ C::swz(ld_row[u])) * 8);
-    ld_lds[u] = (ld_isv[u] ? C::TILE_BYTES : 0) + blk * 1024;
-    ld_off[u] = (uint32_t)(ld_row[u] * (int)(ld_isv[u] ? a.v_ss : a.k_ss) + ld_col[u]) * 2u;
+    ld_lds[u] = (is_v(u) ? C::TILE_BYTES : 0) + blk * 1024;
+    ld_off[u] = (uint32_t)(ld_row[u] * (int)(is_v(u) ? a.v_ss : a.k_ss) + ld_col[u]) * 2u;
   }
 
   // LDS read offsets (bytes, relative to a buffer): K operand for each kc,
@@ -402,13 +405,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_bf16(const AttnArgs 
   }
   bool cp_seg0 = nt0 > 0;               // cursor in the first segment
   int cp_left = cp_seg0 ? nt0 : nt1;     // tiles left in the cursor's segment
-
-  // Whether copy u of this wave is a V block: a compile-time fact when the
-  // tile's blocks split evenly over the waves (K blocks first).
-  auto is_v = [&](int u) {
-    if constexpr (C::BLOCKS % NW == 0) return u >= C::CPW / 2;
-    else return ld_isv[u];
-  };
 
   // Copy the next tile (K and V) into LDS buffer `buf` and advance the
   // cursor.  Only a segment's last tile can be ragged: its rows past the
@@ -447,17 +443,18 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_bf16(const AttnArgs 
   };
   const int fm0 = first_masked(sr0), fm1 = first_masked(sr1);
 
-  auto s_mfma = [&](int buf, f32x16 &s, int kc0, int kc1) {
+  // One stage: tile ti sits in buffer bc.  After the S products the next
+  // copy (tile ti+PF into buffer bl, which every wave finished reading before
+  // this stage's barrier) is issued, so its address work overlaps the
+  // matrix cores.
+  auto step = [&](int ti, int bc, bool copy, int bl) {
+    f32x16 s = f32x16{};
 #pragma unroll
-    for (int kc = kc0; kc < kc1; ++kc) {
-      const bf16x8 ka = *(const lds_bf16x8 *)(bufp(buf) + koff[kc]);
+    for (int kc = 0; kc < D / 16; ++kc) {
+      const bf16x8 ka = *(const lds_bf16x8 *)(bufp(bc) + koff[kc]);
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kc], s, 0, 0, 0);
     }
-  };
-
-  // Softmax of tile ti (scores in s) interleaved with the S MFMAs of tile
-  // ti+1 (K in buffer bn), then P*V for tile ti (V in buffer bc).
-  auto step = [&](f32x16 &s, int ti, int bc, int bn, f32x16 &s_next) {
+    if (copy) issue_next(bl);
     const bool seg1 = ti >= nt0;
     const int kb = (seg1 ? sr1.lo + (ti - nt0) * C::KT : sr0.lo + ti * C::KT);
     if (kb >= (seg1 ? fm1 : fm0)) {
@@ -471,8 +468,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_bf16(const AttnArgs 
         s[r] = key < lim ? s[r] : neg_inf();
       }
     }
-    s_next = f32x16{};
-    s_mfma(bn, s_next, 0, 2);
     float mx = __builtin_fmaxf(__builtin_fmaxf(s[0], s[1]), s[2]);
 #pragma unroll
     for (int r = 3; r < 15; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s[r]), s[r + 1]);
@@ -490,7 +485,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_bf16(const AttnArgs 
         for (int r = 0; r < 16; ++r) acc[mb][r] *= alpha;
     }
     const float moff = (m_run == neg_inf()) ? 0.0f : m_run;
-    s_mfma(bn, s_next, 2, D / 16);
 
     // P = exp2(s * scale_log2 - m): fp32 for the row sum, bf16 (RNE) for P*V.
     bf16x8 pb[2];
@@ -520,65 +514,28 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_fwd_bf16(const AttnArgs 
     }
   };
 
-  f32x16 s_a = f32x16{}, s_b = f32x16{};
-  // Tiles are copied PF = NBUF-1 tiles ahead of use.  Copies complete in
-  // order, so "tile j+1 has landed" is "at most (copies issued after it) are
-  // still outstanding": wait_vm(t) waits until at most the copies of t tiles
-  // (t * CPW instructions per wave) remain.
-  constexpr int PF = NBUF - 1;
-  auto wait_vm = [&](int tiles_after) {
-    // at most n = tiles_after * CPW copies may remain; s_waitcnt takes an
-    // immediate, so dispatch on n (never rounding up)
-    const int n = tiles_after * C::CPW;
-    switch (n) {
-      case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-      case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
-      case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
-      case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
-      case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
-      case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
-      case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
-      case 7: asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
-      case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
-      case 9: asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); break;
-      case 10: asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
-      case 11: asm volatile("s_waitcnt vmcnt(11)" ::: "memory"); break;
-      case 12: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
-      default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;  // never reached (PF <= 7)
+  // Tiles are copied PF tiles ahead of use.  Copies complete in order, so
+  // "tile ti has landed" is "at most the copies issued after it are still
+  // outstanding": (PF - 1) tiles of CPW instructions each.
+  static_assert((C::PF - 1) * C::CPW == 4 || (C::PF - 1) * C::CPW == 2, "wait immediates below");
+  auto wait_tile = [&](int ti) {
+    if (ti + C::PF - 1 < ntiles) {
+      if constexpr ((C::PF - 1) * C::CPW == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    } else {  // the last tiles: nothing was issued after them
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
   };
-  static_assert((NBUF - 3) * C::CPW <= 12, "wait_vm covers at most 12 outstanding copies");
-  if (ntiles > 0) {
-    const int npro = min(ntiles, PF);
-    for (int j = 0; j < npro; ++j) issue_next(j);
-    // tiles 0 and 1 must be in LDS; later ones may still be in flight
-    wait_vm(max(0, npro - 2));
-    lds_barrier();
-    s_mfma(0, s_a, 0, D / 16);
-  }
 
-  // One pipeline stage for tile ti (buffer bc = ti % NBUF): tile ti+1 (buffer
-  // bn) must have landed; tiles ti+2 .. ti+PF-1 may still be in flight (in
-  // the last two stages the wait is simply for every copy).  After the
-  // barrier every wave is done with tile ti-1's buffer (bl), which receives
-  // the copy of tile ti+PF.
-  auto stage = [&](int ti, int bc, int bn, int bl, f32x16 &s_cur, f32x16 &s_nxt) {
-    if (ti + PF - 1 < ntiles)
-      wait_vm(PF - 2);
-    else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    lds_barrier();
-    if (ti + PF < ntiles) issue_next(bl);
-    step(s_cur, ti, bc, bn, s_nxt);
-  };
-
-  for (int ti = 0; ti < ntiles; ti += NBUF) {
+  const int npro = min(ntiles, C::PF);
+  for (int j = 0; j < npro; ++j) issue_next(j);
+  for (int ti = 0; ti < ntiles; ti += C::NBUF) {
 #pragma unroll
-    for (int k = 0; k < NBUF; k += 2) {
+    for (int k = 0; k < C::NBUF; ++k) {
       if (ti + k >= ntiles) break;
-      stage(ti + k, k, (k + 1) % NBUF, (k + NBUF - 1) % NBUF, s_a, s_b);
-      if (ti + k + 1 >= ntiles) break;
-      stage(ti + k + 1, k + 1, (k + 2) % NBUF, k, s_b, s_a);
+      wait_tile(ti + k);
+      lds_barrier();
+      step(ti + k, k, ti + k + C::PF < ntiles, (k + C::PF) % C::NBUF);
     }
   }
 
@@ -951,12 +908,12 @@ static int set_lds(K kernel, size_t bytes, bool &done) {
   return 0;
 }
 
-template <int D, int NW, int NBUF, bool NT>
+template <int D, bool NT>
 static int launch_bf16(const AttnArgs &a, dim3 grid, hipStream_t s) {
   static bool done = false;
-  const int rc = set_lds(attn_fwd_bf16<D, NW, NBUF, NT>, Bf16Cfg<D, NW, NBUF>::LDS_BYTES, done);
+  const int rc = set_lds(attn_fwd_bf16<D, NT>, Bf16Cfg<D>::LDS_BYTES, done);
   if (rc) return rc;
-  attn_fwd_bf16<D, NW, NBUF, NT><<<grid, dim3(64 * NW), Bf16Cfg<D, NW, NBUF>::LDS_BYTES, s>>>(a);
+  attn_fwd_bf16<D, NT><<<grid, dim3(Bf16Cfg<D>::THREADS), Bf16Cfg<D>::LDS_BYTES, s>>>(a);
   return 0;
 }
 
@@ -969,7 +926,7 @@ static int launch_f32(const AttnArgs &a, dim3 grid, dim3 block, hipStream_t s) {
   return 0;
 }
 
-int launch_attn(const AttnArgs &a, int dtype, int head_dim, int nw, void *stream) {
+int launch_attn(const AttnArgs &a, int dtype, int head_dim, void *stream) {
   const dim3 grid(a.per_xcd * 8), block(kThreads);
   hipStream_t s = (hipStream_t)stream;
   int rc;
@@ -978,12 +935,10 @@ int launch_attn(const AttnArgs &a, int dtype, int head_dim, int nw, void *stream
     // query heads of a K/V head packed into it, e.g. decode): stream them.
     bool streamed = a.GP == a.G;
     for (int i = 0; i < a.nitems; ++i) streamed = streamed && a.items[i].nqt == 1;
-    if (nw == 8)
-      rc = head_dim == 128 ? launch_bf16<128, 8, 4, false>(a, grid, s) : launch_bf16<64, 8, 4, false>(a, grid, s);
-    else if (streamed)
-      rc = head_dim == 128 ? launch_bf16<128, 4, 4, true>(a, grid, s) : launch_bf16<64, 4, 4, true>(a, grid, s);
+    if (streamed)
+      rc = head_dim == 128 ? launch_bf16<128, true>(a, grid, s) : launch_bf16<64, true>(a, grid, s);
     else
-      rc = head_dim == 128 ? launch_bf16<128, 4, 4, false>(a, grid, s) : launch_bf16<64, 4, 4, false>(a, grid, s);
+      rc = head_dim == 128 ? launch_bf16<128, false>(a, grid, s) : launch_bf16<64, false>(a, grid, s);
   } else {
     rc = head_dim == 128 ? launch_f32<128>(a, grid, block, s) : launch_f32<64>(a, grid, block, s);
   }
