@@ -330,6 +330,10 @@ __global__ __launch_bounds__(Bf16Cfg<D>::THREADS, Bf16Cfg<D>::OCC) void attn_fwd
   const int qpos = it.qpos0 + (row_ok ? prow : rows_total - 1) / a.GP;
   const int wave_qpos_min = it.qpos0 + min(wave_row0, rows_total - 1) / a.GP;
   const int tile_qpos_max = it.qpos0 + (min(tile_row0 + C::QT, rows_total) - 1) / a.GP;
+  // On the streamed (decode) shape a tile can hold fewer packed rows than
+  // the work-group: a wave whose 32 rows are all past the item only copies.
+  // (Elsewhere the branch costs more than the rare idle wave saves.)
+  const bool wave_live = !NT || wave_row0 < rows_total;
 
   // Q fragment (B operand of S^T = K Q^T): d = 16*kc + 8*g + 0..7.
   bf16x8 qf[D / 16];
@@ -448,6 +452,10 @@ __global__ __launch_bounds__(Bf16Cfg<D>::THREADS, Bf16Cfg<D>::OCC) void attn_fwd
   // this stage's barrier) is issued, so its address work overlaps the
   // matrix cores.
   auto step = [&](int ti, int bc, bool copy, int bl) {
+    if (!wave_live) {  // no valid row: only the copy share
+      if (copy) issue_next(bl);
+      return;
+    }
     f32x16 s = f32x16{};
 #pragma unroll
     for (int kc = 0; kc < D / 16; ++kc) {
