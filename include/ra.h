@@ -184,12 +184,20 @@ ra_status ra_merge(ra_tensor *out, ra_tensor *lse, const ra_tensor *block_out,
  * For every layout except KV_SHARDED, Sq == Sk and S % P == 0 (CONTIG*) or
  * S % 2P == 0 (ZIGZAG).  Rows owned by the emulated rank(s) are written
  * (initialised by the first step, then merged step by step); other rows are
- * untouched.  1 <= P <= 16. */
+ * untouched.  1 <= P <= 16.
+ * KV_SHARDED with fuse_merge = 1, when one block's query tiles cannot fill
+ * the chip (decode): the P blocks' partials do not depend on each other, so
+ * all of them run in one launch, each block cut into sub-blocks, and one
+ * reduction combines every partial into (out, lse) in closed form -- the
+ * gather-merge of the ranks' partials, equal to folding them with the merge
+ * rule in plan order up to rounding.  The workspace then holds the partials
+ * (ra_ring_workspace_bytes). */
 ra_status ra_ring_forward(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v, int P,
                           const ra_layout *layout, ra_tensor *out, ra_tensor *lse,
                           void *stream);
 
-/* Bytes of workspace ra_ring_forward needs for these shapes (0 when fused). */
+/* Bytes of workspace ra_ring_forward needs for these shapes: block results
+ * when unfused, split-K partials for KV_SHARDED decode shapes, else 0. */
 size_t ra_ring_workspace_bytes(const ra_tensor *q, const ra_tensor *k, int P,
                                const ra_layout *layout);
 

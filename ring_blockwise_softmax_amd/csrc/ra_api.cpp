@@ -285,6 +285,76 @@ size_t single_item_ws(int dtype, int64_t B, int64_t Hq, int GP, int64_t q_len, i
   return split_bytes(choose_split(wgs, kv_len, geo.KT), B, Hq, q_len, D);
 }
 
+// KV-sharded, fused: the P blocks are the ranks' shards.  Their partials do
+// not depend on each other (each rank attends the broadcast queries to its
+// own shard), so when one block alone cannot fill the chip all of them run
+// in one launch, each cut into nsub sub-blocks, and one reduction merges the
+// P * nsub partials into (out, lse): the gather-merge.  Returns nsub = 0 when
+// the step-by-step path is used instead (enough work per block, or P = 1).
+Split choose_gather(int64_t wgs, int64_t block_len, int P, int KT) {
+  Split g;
+  g.nsplit = 0;
+  const int64_t target = 2 * 256;
+  if (P < 2 || wgs >= target || block_len < 2 * KT) return g;
+  const int64_t want = (target + wgs - 1) / wgs;  // partials per row over all blocks
+  int64_t ns = std::max<int64_t>(1, (want + P - 1) / P);
+  ns = std::min<int64_t>(ns, std::max<int64_t>(1, block_len / (2 * KT)));
+  int64_t len = (block_len + ns - 1) / ns;
+  len = (len + KT - 1) / KT * KT;
+  g.split_len = (int)len;
+  g.nsplit = (int)((block_len + len - 1) / len);
+  return g;
+}
+
+int64_t kv_sharded_wgs(int dtype, int64_t B, int64_t Hq, int GP, int64_t q_len) {
+  const Geometry geo = geometry(dtype);
+  return B * (Hq / GP) * ((q_len * GP + geo.QT - 1) / geo.QT);
+}
+
+size_t gather_ws(const Split &g, int P, int64_t B, int64_t Hq, int64_t q_len, int64_t D) {
+  if (g.nsplit <= 0) return 0;
+  return (size_t)P * g.nsplit * B * Hq * q_len * (D + 1) * sizeof(float);
+}
+
+// One attention launch over every block (partials to the workspace), then
+// one split reduction that writes (out, lse).
+ra_status run_gather(AttnArgs a, const std::vector<ra_plan_item> &items, const Split &g, int dtype, int D,
+                     char *ws, void *stream) {
+  const int P = (int)items.size();
+  const int64_t rows = items[0].q_len;
+  a.nitems = 0;
+  for (int i = 0; i < P; ++i) {
+    KItem k = to_kitem(items[i], items[i].q_start);
+    k.nsplit = g.nsplit;
+    k.split_len = g.split_len;
+    k.split0 = i * g.nsplit;
+    a.items[a.nitems++] = k;
+  }
+  const int nparts = P * g.nsplit;
+  float *po = reinterpret_cast<float *>(ws);
+  float *pl = po + (size_t)nparts * a.B * a.Hq * rows * D;
+  a.part_out = po, a.part_lse = pl, a.part_rows = (int32_t)rows;
+  SplitArgs s{};
+  s.out = a.out, s.lse = a.lse;
+  s.o_sb = a.o_sb, s.o_ss = a.o_ss, s.o_sh = a.o_sh;
+  s.l_sb = a.l_sb, s.l_ss = a.l_ss, s.l_sh = a.l_sh;
+  s.B = a.B, s.H = a.Hq, s.D = D, s.rows = (int32_t)rows, s.nsplit = nparts;
+  s.o_row0 = (int32_t)items[0].q_start;
+  s.mode = kWrite;
+  s.first = 1;
+  s.part_out = po, s.part_lse = pl;
+  a.mode = kSplit;
+  finish_tiles(a, geometry(dtype).QT);
+  {
+    ProfScope ps(RA_KERNEL_ATTN, stream);
+    const int rc = launch_attn(a, dtype, D, stream);
+    if (rc) return hip_fail(rc, "attention launch");
+  }
+  ProfScope ps(RA_KERNEL_SPLIT_REDUCE, stream);
+  const int rc = launch_split_reduce(s, stream);
+  return rc ? hip_fail(rc, "split-reduce launch") : RA_OK;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -417,7 +487,12 @@ size_t ring_ws_bytes(const ra_tensor *q, const ra_tensor *k, int P, const ra_lay
     const Geometry geo = geometry(q->dtype);
     const int G = (int)(q->h / k->h);
     const int GP = choose_gp(q->s, G, geo.QT);
-    bytes += single_item_ws(q->dtype, q->b, q->h, GP, q->s, k->s / P, q->d);
+    const Split g = L->fuse_merge ? choose_gather(kv_sharded_wgs(q->dtype, q->b, q->h, GP, q->s), k->s / P, P, geo.KT)
+                                  : Split{1, 0};
+    if (g.nsplit > 0 && L->fuse_merge)
+      bytes += gather_ws(g, P, q->b, q->h, q->s, q->d);
+    else
+      bytes += single_item_ws(q->dtype, q->b, q->h, GP, q->s, k->s / P, q->d);
   }
   return (bytes + 255) / 256 * 256;
 }
@@ -472,6 +547,15 @@ ra_status ra_ring_forward(const ra_tensor *q, const ra_tensor *k, const ra_tenso
   for (auto &p : rs.items) qlen_max = std::max(qlen_max, p.q_len);
   base.GP = choose_gp(qlen_max, base.G, geometry(dtype).QT);
   const Geometry geo = geometry(dtype);
+
+  if (L->kind == RA_LAYOUT_KV_SHARDED && L->fuse_merge) {
+    const Split g = choose_gather(kv_sharded_wgs(dtype, q->b, q->h, base.GP, q->s), k->s / P, P, geo.KT);
+    if (g.nsplit > 0) {
+      AttnArgs a = base;
+      set_dest(a, (float *)out->data, out->sb, out->ss, out->sh, (float *)lse->data, lse->sb, lse->ss, lse->sh);
+      return run_gather(a, rs.items, g, dtype, D, ws, stream);
+    }
+  }
 
   for (int t = 0; t < P; ++t) {
     std::vector<ra_plan_item> step;

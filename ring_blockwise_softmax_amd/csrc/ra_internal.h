@@ -37,7 +37,7 @@ struct KItem {
   int32_t nseg;       // 1 or 2
   int32_t first;      // 1: overwrite even in kMerge mode
   int32_t work;       // relative work estimate (host side ordering only)
-  int32_t pad;
+  int32_t split0;     // partial index of this item's split 0 (kSplit mode)
   KSeg seg[2];
 };
 

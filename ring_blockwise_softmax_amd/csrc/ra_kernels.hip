@@ -184,7 +184,7 @@ __device__ __forceinline__ void epilogue(const AttnArgs &a, const KItem &it, con
   const float blse = empty ? neg_inf() : (m_run + __log2f(l_tot)) * kLn2;
 
   if (a.mode == kSplit) {
-    const int64_t prow_idx = ((int64_t)(t.split * a.B + t.b) * a.Hq + h) * a.part_rows + tok;
+    const int64_t prow_idx = ((int64_t)((it.split0 + t.split) * a.B + t.b) * a.Hq + h) * a.part_rows + tok;
     float *po = a.part_out + prow_idx * D;
 #pragma unroll
     for (int mb = 0; mb < D / 32; ++mb)

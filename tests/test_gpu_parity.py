@@ -227,6 +227,41 @@ def test_kv_sharded_decode(fuse):
     compare(f"decode fuse={fuse}", out, lse, ro, rl, "bf16")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("order", ["ring", "tokenring"])
+def test_kv_sharded_gather_ragged(dtype, order):
+    """Fused KV-sharded step with every block's partials gathered in one launch:
+    3 queries, GQA 8/2 (heads packed into tile rows), 7 blocks of 1000 keys
+    (sub-blocks end mid-tile), against one-shot attention."""
+    ra = _ra()
+    import torch
+    q, k, v = _inputs(2, 3, 7000, 8, 2, 128, dtype, seed=57)
+    out, lse = ra.ring_forward(q, k, v, 7, layout="kv_sharded", order=order, fuse_merge=True)
+    torch.cuda.synchronize()
+    ro, rl = attention(q.cpu(), k.cpu(), v.cpu())
+    compare(f"gather ragged {dtype} {order}", out, lse, ro, rl, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_kv_sharded_gather_matches_stepwise(dtype):
+    """The gather-merge (fused) and the step-by-step merge through block_out
+    (unfused) agree on the decode shape.  The two cut the keys differently,
+    so in bf16 each probability is rounded against a different running max:
+    each path's out is within 2^-9 * max|v| of the unrounded weighted mean
+    (|P~ - P| <= 2^-9 P and sum P / l = 1), so they differ by at most twice
+    that.  In fp32 nothing is rounded to a narrower type and the two agree to
+    fp32 accumulation order."""
+    ra = _ra()
+    import torch
+    q, k, v = _inputs(4, 1, 16384, 32, 1, 128, dtype, seed=58)
+    o1, l1 = ra.ring_forward(q, k, v, 8, layout="kv_sharded", fuse_merge=True)
+    o2, l2 = ra.ring_forward(q, k, v, 8, layout="kv_sharded", fuse_merge=False)
+    torch.cuda.synchronize()
+    tol = 1e-5 if dtype == "f32" else 2 * 2.0 ** -9 * v.float().abs().max().item()
+    assert (o1 - o2).abs().max().item() <= tol
+    assert (l1 - l2).abs().max().item() <= 1e-5
+
+
 def test_oracle_ring_emulation_matches_gpu_ring():
     """The oracle's own ring emulation (blockwise) and the GPU agree too."""
     ra = _ra()

@@ -137,6 +137,12 @@ def test_workspace_queries():
     q = T(16, 1, 32, 128)
     k = T(16, 262144, 1, 128)
     assert lib.ra_block_attn_workspace_bytes(ctypes.byref(q), ctypes.byref(k)) > 0
+    # fused KV-sharded decode gathers every block's sub-block partials at once:
+    # 16 query tiles need 32 partials per row to cover the chip twice, i.e. 4
+    # sub-blocks of 8192 keys in each of the 8 blocks
+    kvs = L.RaLayout(3, 0, -1, 1, None, 0)
+    n = lib.ra_ring_workspace_bytes(ctypes.byref(q), ctypes.byref(k), 8, ctypes.byref(kvs))
+    assert n == 8 * 4 * 16 * 32 * 1 * (128 + 1) * 4
 
 
 def test_merge_rejects():
