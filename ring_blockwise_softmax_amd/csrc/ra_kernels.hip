@@ -50,6 +50,7 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 constexpr int kThreads = 256;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
+constexpr float kProbSumLimit = 256.0f;    // 2^kRescaleThreshold
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
@@ -355,6 +356,7 @@ __global__ __launch_bounds__(Bf16Cfg<D>::THREADS, Bf16Cfg<D>::OCC) void attn_fwd
   for (int mb = 0; mb < D / 32; ++mb) acc[mb] = f32x16{};
   float m_run = neg_inf();
   float l_part = 0.0f;
+  bool ref_ok = false;  // wave-uniform: every lane's m_run is finite
 
   // Key tiles of the (up to two) segments, flattened.
   const SegRange sr0 = seg_range(it, 0, t.split, tile_qpos_max);
@@ -476,38 +478,58 @@ __global__ __launch_bounds__(Bf16Cfg<D>::THREADS, Bf16Cfg<D>::OCC) void attn_fwd
         s[r] = key < lim ? s[r] : neg_inf();
       }
     }
-    float mx = __builtin_fmaxf(__builtin_fmaxf(s[0], s[1]), s[2]);
-#pragma unroll
-    for (int r = 3; r < 15; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s[r]), s[r + 1]);
-    mx = __builtin_fmaxf(mx, s[15]);
-    mx = max_halves(mx) * a.scale_log2;
-    const float m_new = fmaxf(m_run, mx);
-    const bool need = m_new > m_run + kRescaleThreshold;
-    if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
-      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-      m_run = need ? m_new : m_run;
-      l_part *= alpha;
-#pragma unroll
-      for (int mb = 0; mb < D / 32; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[mb][r] *= alpha;
-    }
-    const float moff = (m_run == neg_inf()) ? 0.0f : m_run;
-
     // P = exp2(s * scale_log2 - m): fp32 for the row sum, bf16 (RNE) for P*V.
+    // Returns this lane's sum of the tile's 16 probabilities.
     bf16x8 pb[2];
+    auto exps = [&](float moff) {
+      float t = 0.0f;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
+      for (int c = 0; c < 2; ++c) {
 #pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * c + e], a.scale_log2, -moff));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * c + e + 1], a.scale_log2, -moff));
-        const bf16x2 pp = {(bf16)p0, (bf16)p1};
-        pb[c][e] = pp[0];
-        pb[c][e + 1] = pp[1];
-        l_part += p0 + p1;
+        for (int e = 0; e < 8; e += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * c + e], a.scale_log2, -moff));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * c + e + 1], a.scale_log2, -moff));
+          const bf16x2 pp = {(bf16)p0, (bf16)p1};
+          pb[c][e] = pp[0];
+          pb[c][e + 1] = pp[1];
+          t += p0 + p1;
+        }
       }
+      return t;
+    };
+    // Fast path: exponentiate against the running reference m_run without
+    // this tile's maximum.  It stands when every lane has a finite reference
+    // and no lane's probabilities sum past 2^8 (so none exceeds 2^8: no
+    // overflow, and the reference stays within 8 of the row maximum).
+    // Otherwise the tile is redone against its exact maximum, rescaling the
+    // lanes whose maximum grew.
+    float tsum = 0.0f;
+    bool redo = !ref_ok;
+    if (ref_ok) {
+      tsum = exps(m_run);
+      redo = __builtin_amdgcn_ballot_w64(!(tsum <= kProbSumLimit)) != 0;
     }
+    if (__builtin_expect(redo, 0)) {
+      float mx = __builtin_fmaxf(__builtin_fmaxf(s[0], s[1]), s[2]);
+#pragma unroll
+      for (int r = 3; r < 15; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s[r]), s[r + 1]);
+      mx = __builtin_fmaxf(mx, s[15]);
+      mx = max_halves(mx) * a.scale_log2;
+      const float m_new = fmaxf(m_run, mx);
+      const bool need = m_new > m_run;
+      if (__builtin_amdgcn_ballot_w64(need) != 0) {
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+        m_run = need ? m_new : m_run;
+        l_part *= alpha;
+#pragma unroll
+        for (int mb = 0; mb < D / 32; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[mb][r] *= alpha;
+      }
+      tsum = exps(m_run == neg_inf() ? 0.0f : m_run);
+      ref_ok = __builtin_amdgcn_ballot_w64(m_run == neg_inf()) == 0;
+    }
+    l_part += tsum;
     // out^T += V^T P^T over two 16-key chunks (chunk c is 16 rows further).
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
