@@ -10,7 +10,7 @@
 // evaluated in its overflow-free form max(lse, blse) + log1p(exp(-|diff|)).
 //
 // Kernel shape (bf16 path; one work-group = 4 waves = 128 packed query rows,
-// or 8 waves = 256 as a tuning option):
+// three work-groups per CU for d = 128):
 //  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //    the key index runs down the MFMA M dimension and the query index across
 //    N, so each lane owns one query column and the softmax row reductions are
@@ -20,11 +20,13 @@
 //    The V^T A operand comes from the row-major V tile through
 //    ds_read_b64_tr_b16 (16-lane transpose reads), so V is staged as loaded.
 //  * K/V tiles of 32 keys go global -> LDS directly (global_load_lds_dwordx4)
-//    into a 4-deep ring, three tiles ahead of use, one barrier per tile; the
-//    S products of tile j+1 are issued while the softmax of tile j runs.
-//  * Online softmax in the exp2 domain with a lazy rescale: the running
-//    maximum used for exponentiation only moves when a row's maximum grows
-//    by more than 2^8, so the accumulator is rarely rescaled; the final
+//    into a 3-deep ring, two tiles ahead of use, one barrier per tile.  Each
+//    stage runs S, softmax and P*V of its tile in order; the three resident
+//    work-groups per CU overlap one another's phases instead.
+//  * Online softmax in the exp2 domain against a running reference: a tile
+//    is exponentiated against the row's current reference without taking its
+//    maximum first, and redone against its exact maximum only when some row
+//    lacks a reference or its probabilities sum past 2^8.  The final
 //    normalisation uses the same reference, so the result is unchanged.
 //  * Work tiles are assigned XCD-contiguously: consecutive tiles of one
 //    (batch, head) land on the same XCD and share its L2 copy of K/V.
@@ -49,8 +51,8 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kThreads = 256;
 constexpr float kLn2 = 0.69314718055994530942f;
-constexpr float kRescaleThreshold = 8.0f;  // log2 units
-constexpr float kProbSumLimit = 256.0f;    // 2^kRescaleThreshold
+constexpr float kRescaleThreshold = 8.0f;  // log2 units (fp32 kernel's lazy rescale)
+constexpr float kProbSumLimit = 256.0f;    // 2^kRescaleThreshold: bf16 fast-path bound
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
