@@ -289,7 +289,7 @@ size_t single_item_ws(int dtype, int64_t B, int64_t Hq, int GP, int64_t q_len, i
 // not depend on each other (each rank attends the broadcast queries to its
 // own shard), so when one block alone cannot fill the chip all of them run
 // in one launch, each cut into nsub sub-blocks, and one reduction merges the
-// P * nsub partials into (out, lse): the gather-merge.  Returns nsub = 0 when
+// P * nsub partials into (out, lse): the gather-merge.  Returns nsplit = 0 when
 // the step-by-step path is used instead (enough work per block, or P = 1).
 Split choose_gather(int64_t wgs, int64_t block_len, int P, int KT) {
   Split g;
