@@ -231,7 +231,7 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the ring is emulated in one device's memory; "
-              "--gpus above 1 is not supported by this build.", file=sys.stderr)
+              "--gpus above 1 is not supported.", file=sys.stderr)
         sys.exit(2)
 
     import torch
