@@ -10,11 +10,17 @@ before timing starts.
 Prints ONE JSON line.  Extra objects:
   roofline      -- the attention kernel: algorithmic flops per launch divided
                    by its average launch time (HIP events on the launch stream
-                   during the timed region), against the bf16 dense MFMA peak.
+                   during the timed region), against the bf16 dense MFMA peak;
+                   for the decode workload, K/V (+Q) bytes per launch against
+                   the HBM peak.
+  step_ms       -- min / median / max of per-step times (one event pair per
+                   step, a separate region from the timed one).
   merge         -- the standalone merge kernel at the GQA 1M-token share shape
                    (4,194,304 row-heads x d128, 6.49 GB moved), in GB/s.
   cpu_baseline  -- the fp64 CPU oracle on a bounded sample of the same
-                   workload (query rows x all keys), scaled to TFLOP/s.
+                   workload (query rows x all keys), scaled to TFLOP/s; its
+                   "check" compares the GPU result on those rows with the
+                   oracle's (max abs errors, max |oracle out|).
 """
 
 from __future__ import annotations
@@ -93,8 +99,27 @@ def flops_of(w, rank=None):
     return 4.0 * w.head_dim * w.heads_q * w.batch * visible_pairs(w, rank)
 
 
-def cpu_baseline(w, q, k, v, budget_s=12.0):
-    """Time the oracle on a bounded sample of query rows against all keys."""
+def owned_rows(w, rank):
+    """Query rows whose (out, lse) the emulated rank(s) produce."""
+    import numpy as np
+
+    S, P = w.seq_q, w.P
+    if rank is None or rank < 0 or w.layout == "kv_sharded":
+        return np.arange(S)
+    if w.layout == "zigzag_causal":
+        c = S // (2 * P)
+        return np.concatenate([np.arange(rank * c, (rank + 1) * c),
+                               np.arange((2 * P - 1 - rank) * c, (2 * P - rank) * c)])
+    n = S // P
+    return np.arange(rank * n, (rank + 1) * n)
+
+
+def cpu_baseline(w, q, k, v, out=None, lse=None, rank=None, budget_s=12.0):
+    """Time the oracle on a bounded sample of query rows against all keys.
+
+    When the GPU result (out, lse) is given, the same sampled rows are also
+    compared with the oracle's values (max abs errors and max |oracle out|).
+    """
     import numpy as np
 
     from oracle import attention
@@ -108,15 +133,23 @@ def cpu_baseline(w, q, k, v, budget_s=12.0):
     kc, vc = k.cpu(), v.cpu()
     causal = w.layout != "contig" and w.layout != "kv_sharded"
     S = w.seq_q
+    pool = owned_rows(w, rank)
     rng = np.random.default_rng(0)
     rows = 16
     total_rows, total_t = 0, 0.0
-    while total_t < budget_s and total_rows < S:
-        sel = np.sort(rng.choice(S, size=min(rows, S), replace=False))
+    err_out = err_lse = max_ref = 0.0
+    while total_t < budget_s and total_rows < len(pool):
+        sel = np.sort(rng.choice(pool, size=min(rows, len(pool)), replace=False))
         qs = q[:, sel].cpu()
         t0 = time.perf_counter()
-        attention(qs, kc, vc, causal=causal, q_pos=sel)
+        ro, rl = attention(qs, kc, vc, causal=causal, q_pos=sel)
         dt = time.perf_counter() - t0
+        if out is not None:
+            go = out[:, sel].double().cpu().numpy()
+            gl = lse[:, :, sel].double().cpu().numpy()
+            err_out = max(err_out, float(np.max(np.abs(go - ro))))
+            err_lse = max(err_lse, float(np.max(np.abs(gl - rl))))
+            max_ref = max(max_ref, float(np.max(np.abs(ro))))
         total_rows += len(sel)
         total_t += dt
         rows = min(rows * 2, 4096)
@@ -126,7 +159,7 @@ def cpu_baseline(w, q, k, v, budget_s=12.0):
     # the workload's mean keys per row otherwise
     keys_per_row = visible_pairs(w) / (w.seq_q * 1.0) if causal else w.seq_k
     fl = 4.0 * w.head_dim * w.heads_q * w.batch * total_rows * keys_per_row
-    return {
+    rec = {
         "value": fl / total_t / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
@@ -134,6 +167,10 @@ def cpu_baseline(w, q, k, v, budget_s=12.0):
         "sample": f"{total_rows} query rows x {w.heads_q} heads x all {w.seq_k} keys "
                   f"(of {w.seq_q} rows), fp64 numpy, {total_t:.1f} s",
     }
+    if out is not None:
+        rec["check"] = {"rows": total_rows, "max_err_out": err_out, "max_abs_oracle_out": max_ref,
+                        "max_err_lse": err_lse}
+    return rec
 
 
 def merge_bench(steps=10):
@@ -218,7 +255,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up steps (default: at least 3 and at least 0.3 s of steps, "
+                         "so the clocks settle on short workloads too)")
     ap.add_argument("--workload", default="mha24k")
     ap.add_argument("--order", default="ring", choices=["ring", "tokenring"])
     ap.add_argument("--unfused", action="store_true", help="separate merge kernel")
@@ -244,9 +283,18 @@ def main():
     q, k, v = make_inputs(w, device="cuda")
     runner = ra.RingRunner(q, k, v, w.P, layout=w.layout, order=args.order, rank=rank,
                            fuse_merge=not args.unfused)
-    for _ in range(args.warmup):
-        runner.run()
-    torch.cuda.synchronize()
+    if args.warmup is not None:
+        for _ in range(args.warmup):
+            runner.run()
+        torch.cuda.synchronize()
+    else:
+        args.warmup, t0 = 0, time.perf_counter()
+        while args.warmup < 3 or time.perf_counter() - t0 < 0.3:
+            runner.run()
+            args.warmup += 1
+            if args.warmup % 3 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
 
     # Timed region 1: the steps alone (bracketed by synchronisation).
     stream = torch.cuda.current_stream()
@@ -267,6 +315,14 @@ def main():
     torch.cuda.synchronize()
     prof = ra.profile_read()
     ra.profile_enable(False)
+    # Timed region 3: one event pair per step, for the spread over steps.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in evs:
+        a.record(stream)
+        runner.run()
+        b.record(stream)
+    torch.cuda.synchronize()
+    per_step = sorted(a.elapsed_time(b) for a, b in evs)
 
     total_flops = flops_of(w, rank)
     tflops = total_flops / (ms_step / 1e3) / 1e12
@@ -276,6 +332,18 @@ def main():
     flops_per_launch = total_flops / launches_per_step
     achieved = flops_per_launch / (attn_avg_ms / 1e3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
+    if w.layout == "kv_sharded":
+        # decode: the attention launch streams K and V once (plus the queries)
+        esz = q.element_size()
+        kv_bytes = 2 * w.batch * w.seq_k * w.heads_kv * w.head_dim * esz
+        q_bytes = w.batch * w.seq_q * w.heads_q * w.head_dim * esz
+        bytes_per_launch = (kv_bytes + q_bytes) / launches_per_step
+        roof = {"bound": "hbm", "achieved": round(bytes_per_launch / (attn_avg_ms / 1e3) / 1e9, 2),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "algorithmic_bytes_per_launch": bytes_per_launch}
+        roof["frac"] = round(roof["achieved"] / PEAK_HBM_GBS, 4)
+    else:
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "flops_per_launch": flops_per_launch}
 
     rec = {
         "metric": "attention TFLOP/s + % bf16 MFMA peak at S=24000, H=32, d=128, 1 GPU",
@@ -304,17 +372,23 @@ def main():
         },
         "pct_peak": round(100.0 * tflops / peak, 2),
         "roofline": {
-            "bound": "mfma",
-            "kernel": "attn_fwd_bf16<128> (fused merge epilogue)" if w.dtype == "bf16" else "attn_fwd_f32",
-            "achieved": round(achieved, 2),
-            "peak": peak,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / peak, 4),
+            "bound": roof["bound"],
+            "kernel": ("attn_fwd_bf16<%d>" % w.head_dim if w.dtype == "bf16" else "attn_fwd_f32<%d>" % w.head_dim)
+                      + (" (partials for the gather-merge)" if w.layout == "kv_sharded"
+                         else " (fused merge epilogue)" if not args.unfused else ""),
+            "achieved": roof["achieved"],
+            "peak": roof["peak"],
+            "unit": roof["unit"],
+            "frac": roof["frac"],
             "traffic": measured_traffic(w.name),
             "launches_per_step": launches_per_step,
             "avg_launch_ms": round(attn_avg_ms, 4),
-            "flops_per_launch": flops_per_launch,
+            **{k_: v_ for k_, v_ in roof.items() if k_ in ("flops_per_launch", "algorithmic_bytes_per_launch")},
         },
+        "step_ms": {"min": round(per_step[0], 4), "median": round(per_step[len(per_step) // 2], 4),
+                    "max": round(per_step[-1], 4)},
+        "seed": w.seed,
+        "hip": torch.version.hip,
     }
     if args.calib_copy:
         src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda")
@@ -326,7 +400,7 @@ def main():
     if not args.no_merge:
         rec["merge"] = merge_bench()
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(w, q, k, v)
+        rec["cpu_baseline"] = cpu_baseline(w, q, k, v, runner.out, runner.lse, rank)
     print(json.dumps(rec), flush=True)
 
 

@@ -1,0 +1,51 @@
+"""Host-side accounting of bench.py, pinned to the workload definitions.
+
+The flop counts are the visible (query, key) pairs times 4*d*Hq*B; the
+closed forms for the zigzag rank share (2Pc^2 + c pairs) are checked against
+a brute-force sum over the rows that rank owns.
+"""
+
+import numpy as np
+import pytest
+
+import bench
+from ring_blockwise_softmax_amd.workloads import WORKLOADS
+
+
+def test_mha24k_flops():
+    w = WORKLOADS["mha24k"]
+    assert bench.flops_of(w) == 4.0 * 128 * 32 * 4 * 6000 * 24000 == 9437184000000.0
+    assert bench.flops_of(w, rank=0) == 4.0 * 128 * 32 * 6000 * 24000
+
+
+@pytest.mark.parametrize("name", ["zigzag24k", "gqa1m"])
+def test_zigzag_rank_share_pairs_brute_force(name):
+    w = WORKLOADS[name]
+    c = w.seq_q // (2 * w.P)
+    for rank in (0, w.P - 1):
+        rows = bench.owned_rows(w, rank)
+        assert len(rows) == 2 * c and len(np.unique(rows)) == 2 * c
+        brute = int(np.sum(rows.astype(np.int64) + 1))      # causal: row i sees keys 0..i
+        assert bench.visible_pairs(w, rank) == brute == 2 * w.P * c * c + c
+    # all ranks together own every row once
+    allrows = np.concatenate([bench.owned_rows(w, r) for r in range(w.P)])
+    assert np.array_equal(np.sort(allrows), np.arange(w.seq_q))
+    assert bench.visible_pairs(w) == w.seq_q * (w.seq_q + 1) // 2
+
+
+def test_gqa1m_rank_share_flops():
+    w = WORKLOADS["gqa1m"]
+    assert bench.visible_pairs(w, 0) == 68_719_542_272
+    assert abs(bench.flops_of(w, 0) - 1.1259e15) / 1.1259e15 < 1e-4
+
+
+def test_decode_pairs_and_rows():
+    w = WORKLOADS["mqa_decode"]
+    assert bench.visible_pairs(w) == w.seq_q * w.seq_k
+    assert np.array_equal(bench.owned_rows(w, -1), np.arange(w.seq_q))
+
+
+def test_contig_owned_rows():
+    w = WORKLOADS["mha24k"]
+    n = w.seq_q // w.P
+    assert np.array_equal(bench.owned_rows(w, 2), np.arange(2 * n, 3 * n))
