@@ -114,6 +114,17 @@ def owned_rows(w, rank):
     return np.arange(rank * n, (rank + 1) * n)
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, q, k, v, out=None, lse=None, rank=None, budget_s=12.0):
     """Time the oracle on a bounded sample of query rows against all keys.
 
@@ -166,7 +177,22 @@ def cpu_baseline(w, q, k, v, out=None, lse=None, rank=None, budget_s=12.0):
         "kind": "oracle",
         "sample": f"{total_rows} query rows x {w.heads_q} heads x all {w.seq_k} keys "
                   f"(of {w.seq_q} rows), fp64 numpy, {total_t:.1f} s",
+        "cpu": cpu_model(),
     }
+    # one single-threaded run of the oracle on the first sampled rows
+    try:
+        from threadpoolctl import threadpool_limits
+
+        sel = np.sort(rng.choice(pool, size=min(16, len(pool)), replace=False))
+        qs = q[:, sel].cpu()
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            attention(qs, kc, vc, causal=causal, q_pos=sel)
+            dt1 = time.perf_counter() - t0
+        rec["single_thread"] = {"value": 4.0 * w.head_dim * w.heads_q * w.batch * len(sel) * keys_per_row / dt1 / 1e12,
+                                "unit": "TFLOP/s", "sample": f"{len(sel)} query rows, {dt1:.1f} s"}
+    except ImportError:
+        pass
     if out is not None:
         rec["check"] = {"rows": total_rows, "max_err_out": err_out, "max_abs_oracle_out": max_ref,
                         "max_err_lse": err_lse}
