@@ -105,12 +105,22 @@ typedef struct ra_tensor {
  *                    pairs skipped.
  *   KV_SHARDED:      queries are not partitioned (one owner, e.g. a decode
  *                    step with Sq != Sk); K/V is cut into P contiguous blocks,
- *                    each visited once; non-causal. */
+ *                    each visited once; non-causal.
+ *   KV_SHARDED_CAUSAL: as KV_SHARDED, but the queries are the last Sq of the
+ *                    Sk tokens (query i sits at position Sk - Sq + i: a prefill
+ *                    chunk or decode step against a sharded cache) and the
+ *                    causal mask applies on those positions (bottom-right
+ *                    aligned).  Needs Sq <= Sk.  Block 0 is visible to every
+ *                    query, so each row has a partial from the first step.
+ *                    (TokenRing review, "Reading between the lines": the
+ *                    decode / chunked-prefill extension with K/V kept in place
+ *                    and partials returned to the query owner.) */
 typedef enum ra_layout_kind {
   RA_LAYOUT_CONTIG = 0,
   RA_LAYOUT_CONTIG_CAUSAL = 1,
   RA_LAYOUT_ZIGZAG_CAUSAL = 2,
-  RA_LAYOUT_KV_SHARDED = 3
+  RA_LAYOUT_KV_SHARDED = 3,
+  RA_LAYOUT_KV_SHARDED_CAUSAL = 4
 } ra_layout_kind;
 
 /* Merge order of the emulated ring.
@@ -148,6 +158,8 @@ typedef struct ra_plan_item {
   int32_t nseg;              /* 1 or 2                                         */
   int32_t first;             /* 1: first partial for these rows (overwrites)   */
   ra_plan_seg seg[2];
+  int64_t q_pos0;            /* token position of row q_start (= q_start except
+                                for KV_SHARDED_CAUSAL: q_start + Sk - Sq)      */
 } ra_plan_item;
 
 /* ra_block_attn_fwd -- block_out, block_lse of one query block against one

@@ -31,7 +31,7 @@ import numpy as np
 from .attention import attention
 from .merge import merge_stable, merge_literal, merge_bshd
 
-LAYOUTS = ("contig", "contig_causal", "zigzag_causal", "kv_sharded")
+LAYOUTS = ("contig", "contig_causal", "zigzag_causal", "kv_sharded", "kv_sharded_causal")
 
 
 def contiguous_shares(S: int, P: int):
@@ -109,9 +109,13 @@ def ring_blockwise(q, k, v, P: int, layout: str = "contig", order: str = "ring",
     partial into its running pair with the sigma rule.  Rows of ranks not in
     ``ranks`` stay at the identity (0, -inf).
 
-    layout: "contig" | "contig_causal" | "zigzag_causal" | "kv_sharded"
+    layout: "contig" | "contig_causal" | "zigzag_causal" | "kv_sharded" |
+      "kv_sharded_causal"
       ("kv_sharded": queries are not partitioned; K/V is cut into P contiguous
-       blocks, each visited once -- the decode-style shape.)
+       blocks, each visited once -- the decode-style shape.  "kv_sharded_causal":
+       the same, with the queries taken as the last Sq of the Sk positions and
+       the causal mask applied on positions -- a prefill chunk or a decode step
+       at the end of a sharded cache.)
     rule: "stable" (merge_stable) or "literal" (merge_literal; finite only).
     """
     B, Sq, Hq, d = q.shape
@@ -120,11 +124,16 @@ def ring_blockwise(q, k, v, P: int, layout: str = "contig", order: str = "ring",
     out = np.zeros((B, Sq, Hq, d), dtype=np.float64)
     lse = np.full((B, Hq, Sq), -np.inf, dtype=np.float64)
 
-    if layout == "kv_sharded":
+    q_shift = 0
+    if layout in ("kv_sharded", "kv_sharded_causal"):
         q_rows = [np.arange(Sq, dtype=np.int64)]
         kv_rows = contiguous_shares(Sk, P)
         owners = [0]
-        causal = False
+        causal = layout == "kv_sharded_causal"
+        if causal:
+            if Sq > Sk:
+                raise ValueError("kv_sharded_causal needs Sq <= Sk")
+            q_shift = Sk - Sq     # query row i sits at position Sk - Sq + i
     else:
         if Sq != Sk:
             raise ValueError("ring layouts need Sq == Sk")
@@ -137,11 +146,11 @@ def ring_blockwise(q, k, v, P: int, layout: str = "contig", order: str = "ring",
         rr = q_rows[r]
         run_out = np.zeros((B, len(rr), Hq, d))
         run_lse = np.full((B, Hq, len(rr)), -np.inf)
-        kv_order = ring_kv_order(r if layout != "kv_sharded" else 0, P, order)
+        kv_order = ring_kv_order(r if not layout.startswith("kv_sharded") else 0, P, order)
         for s in kv_order:
             kk = kv_rows[s]
             bo, bl = attention(q[:, rr], k[:, kk], v[:, kk], causal=causal,
-                               q_pos=rr, k_pos=kk)
+                               q_pos=rr + q_shift, k_pos=kk)
             if rule == "literal" and not np.all(np.isfinite(run_lse)):
                 # The printed rule is undefined at lse = -inf; the first
                 # block is taken as is (the rule's limit there).

@@ -19,7 +19,7 @@ RA_BF16, RA_F32 = 0, 1
 # ra_mask
 MASKS = {"none": 0, "causal": 1, "causal_bottom_right": 2}
 # ra_layout_kind
-LAYOUTS = {"contig": 0, "contig_causal": 1, "zigzag_causal": 2, "kv_sharded": 3}
+LAYOUTS = {"contig": 0, "contig_causal": 1, "zigzag_causal": 2, "kv_sharded": 3, "kv_sharded_causal": 4}
 ORDERS = {"ring": 0, "tokenring": 1}
 KERNEL_KINDS = ("attn", "merge", "split_reduce")
 
@@ -44,7 +44,7 @@ class RaPlanSeg(ctypes.Structure):
 class RaPlanItem(ctypes.Structure):
     _fields_ = [("step", ctypes.c_int32), ("rank", ctypes.c_int32), ("q_start", ctypes.c_int64),
                 ("q_len", ctypes.c_int64), ("nseg", ctypes.c_int32), ("first", ctypes.c_int32),
-                ("seg", RaPlanSeg * 2)]
+                ("seg", RaPlanSeg * 2), ("q_pos0", ctypes.c_int64)]
 
 
 EXPORTS = {

@@ -131,7 +131,7 @@ def ring_plan(Sq, Sk, P, layout="contig", order="ring", rank=-1):
     items = []
     for it in arr[:n]:
         items.append({
-            "step": it.step, "rank": it.rank, "q_start": it.q_start, "q_len": it.q_len,
+            "step": it.step, "rank": it.rank, "q_start": it.q_start, "q_len": it.q_len, "q_pos0": it.q_pos0,
             "first": bool(it.first),
             "segs": [{"kv_start": it.seg[i].kv_start, "kv_len": it.seg[i].kv_len,
                       "causal": bool(it.seg[i].causal), "kv_rank": it.seg[i].kv_rank}

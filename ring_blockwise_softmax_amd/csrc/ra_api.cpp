@@ -191,7 +191,7 @@ KItem to_kitem(const ra_plan_item &p, int64_t o_row0) {
   KItem k{};
   k.q_start = (int32_t)p.q_start;
   k.q_len = (int32_t)p.q_len;
-  k.qpos0 = (int32_t)p.q_start;
+  k.qpos0 = (int32_t)p.q_pos0;
   k.o_row0 = (int32_t)o_row0;
   k.nsplit = 1;
   k.split_len = 0;
@@ -287,15 +287,24 @@ size_t single_item_ws(int dtype, int64_t B, int64_t Hq, int GP, int64_t q_len, i
 
 // KV-sharded, fused: the P blocks are the ranks' shards.  Their partials do
 // not depend on each other (each rank attends the broadcast queries to its
-// own shard), so when one block alone cannot fill the chip all of them run
-// in one launch, each cut into nsub sub-blocks, and one reduction merges the
-// P * nsub partials into (out, lse): the gather-merge.  Returns nsplit = 0 when
-// the step-by-step path is used instead (enough work per block, or P = 1).
+// own shard), so when one block's query tiles make only a few rounds of
+// work-groups (a launch per block would spend much of its time in its last,
+// partly filled round) all of them run in one launch, each cut into nsub
+// sub-blocks when that is still short of two work-groups per CU, and one
+// reduction merges the P * nsub partials into (out, lse): the gather-merge.
+// Returns nsplit = 0 when the step-by-step path is used instead (P = 1, or
+// at least kGatherMaxWgs work-groups per block).
+constexpr int64_t kGatherMaxWgs = 2048;
 Split choose_gather(int64_t wgs, int64_t block_len, int P, int KT) {
   Split g;
   g.nsplit = 0;
   const int64_t target = 2 * 256;
-  if (P < 2 || wgs >= target || block_len < 2 * KT) return g;
+  if (P < 2 || wgs >= kGatherMaxWgs || block_len < 1) return g;
+  if (wgs >= target || block_len < 2 * KT) {  // no sub-blocks
+    g.nsplit = 1;
+    g.split_len = (int)block_len;
+    return g;
+  }
   const int64_t want = (target + wgs - 1) / wgs;  // partials per row over all blocks
   int64_t ns = std::max<int64_t>(1, (want + P - 1) / P);
   ns = std::min<int64_t>(ns, std::max<int64_t>(1, block_len / (2 * KT)));
@@ -457,9 +466,13 @@ struct RingShape {
   std::vector<ra_plan_item> items;
 };
 
+// Layouts whose queries have one owner and whose K/V blocks are the ranks'
+// shards (decode, chunked prefill).
+bool kv_sharded(int kind) { return kind == RA_LAYOUT_KV_SHARDED || kind == RA_LAYOUT_KV_SHARDED_CAUSAL; }
+
 // Row of the block-result workspace for the first query row of an item.
 int64_t ws_row_of(const ra_layout *L, int P, int64_t S, const ra_plan_item &it) {
-  if (L->rank < 0 || L->kind == RA_LAYOUT_KV_SHARDED) return it.q_start;
+  if (L->rank < 0 || kv_sharded(L->kind)) return it.q_start;
   if (L->kind == RA_LAYOUT_ZIGZAG_CAUSAL) {
     const int64_t c = S / (2 * P);
     return it.q_start == (int64_t)L->rank * c ? 0 : c + (it.q_start - (int64_t)(2 * P - 1 - L->rank) * c);
@@ -473,7 +486,7 @@ ra_status ring_setup(const ra_tensor *q, const ra_tensor *k, int P, const ra_lay
                          (long long)k->s, P, L->kind, L->rank);
   rs.items.resize(n);
   ra_ring_plan(q->s, k->s, P, L, rs.items.data(), n);
-  if (L->kind == RA_LAYOUT_KV_SHARDED || L->rank < 0)
+  if (kv_sharded(L->kind) || L->rank < 0)
     rs.ws_rows = q->s;
   else
     rs.ws_rows = q->s / P;
@@ -483,7 +496,7 @@ ra_status ring_setup(const ra_tensor *q, const ra_tensor *k, int P, const ra_lay
 size_t ring_ws_bytes(const ra_tensor *q, const ra_tensor *k, int P, const ra_layout *L, const RingShape &rs) {
   size_t bytes = 0;
   if (!L->fuse_merge) bytes += (size_t)q->b * rs.ws_rows * q->h * (q->d + 1) * sizeof(float);
-  if (L->kind == RA_LAYOUT_KV_SHARDED) {
+  if (kv_sharded(L->kind)) {
     const Geometry geo = geometry(q->dtype);
     const int G = (int)(q->h / k->h);
     const int GP = choose_gp(q->s, G, geo.QT);
@@ -514,8 +527,10 @@ ra_status ra_ring_forward(const ra_tensor *q, const ra_tensor *k, const ra_tenso
   if ((st = check_qkv(q, k, v)) || (st = check_out(q, out, lse, "out", "lse"))) return st;
   if (!L) return fail(RA_E_INVALID, "null layout");
   if (P < 1 || P > 16) return fail(RA_E_UNSUPPORTED, "P must be in [1, 16]");
-  if (L->kind < RA_LAYOUT_CONTIG || L->kind > RA_LAYOUT_KV_SHARDED) return fail(RA_E_INVALID, "unknown layout kind");
-  if (L->kind != RA_LAYOUT_KV_SHARDED && q->s != k->s) return fail(RA_E_INVALID, "ring layouts need Sq == Sk");
+  if (L->kind < RA_LAYOUT_CONTIG || L->kind > RA_LAYOUT_KV_SHARDED_CAUSAL) return fail(RA_E_INVALID, "unknown layout kind");
+  if (!kv_sharded(L->kind) && q->s != k->s) return fail(RA_E_INVALID, "ring layouts need Sq == Sk");
+  if (L->kind == RA_LAYOUT_KV_SHARDED_CAUSAL && q->s > k->s)
+    return fail(RA_E_INVALID, "KV_SHARDED_CAUSAL needs Sq <= Sk (queries are the last Sq tokens)");
   RingShape rs;
   if ((st = ring_setup(q, k, P, L, rs))) return st;
   const size_t need = ring_ws_bytes(q, k, P, L, rs);
@@ -548,7 +563,7 @@ ra_status ra_ring_forward(const ra_tensor *q, const ra_tensor *k, const ra_tenso
   base.GP = choose_gp(qlen_max, base.G, geometry(dtype).QT);
   const Geometry geo = geometry(dtype);
 
-  if (L->kind == RA_LAYOUT_KV_SHARDED && L->fuse_merge) {
+  if (kv_sharded(L->kind) && L->fuse_merge) {
     const Split g = choose_gather(kv_sharded_wgs(dtype, q->b, q->h, base.GP, q->s), k->s / P, P, geo.KT);
     if (g.nsplit > 0) {
       AttnArgs a = base;
@@ -597,7 +612,7 @@ ra_status ra_ring_forward(const ra_tensor *q, const ra_tensor *k, const ra_tenso
         set_dest(a, (float *)out->data, out->sb, out->ss, out->sh, (float *)lse->data, lse->sb, lse->ss, lse->sh);
       a.mode = (pass == 1 && L->fuse_merge) ? kMerge : kWrite;
 
-      if (a.nitems == 1 && L->kind == RA_LAYOUT_KV_SHARDED) {
+      if (a.nitems == 1 && kv_sharded(L->kind)) {
         if ((st = run_single_item(a, dtype, D, ws_split, ws_split_bytes, stream))) return st;
       } else {
         finish_tiles(a, geo.QT);

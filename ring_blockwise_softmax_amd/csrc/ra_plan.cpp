@@ -15,6 +15,12 @@
 //    chunks r and 2P-1-r.  With the causal mask on global positions, chunk
 //    pair (query chunk a, key chunk b) is full if b < a, lower-triangular if
 //    b == a and fully masked (skipped) if b > a.
+//  * K/V-sharded layouts (TokenRing review, "Reading between the lines": the
+//    decode / chunked-prefill extension): the queries have one owner, each
+//    rank keeps its K/V block and returns its partial to the owner.  In the
+//    causal variant the queries are the last Sq of the Sk positions, so a
+//    block is fully visible when its last key precedes the first query and
+//    causal otherwise; block 0 is visible to every query.
 #include <stdint.h>
 
 #include "ra.h"
@@ -37,6 +43,7 @@ ra_plan_item make_item(int step, int rank, int64_t q0, int64_t qn) {
   it.rank = rank;
   it.q_start = q0;
   it.q_len = qn;
+  it.q_pos0 = q0;
   it.nseg = 0;
   it.first = 0;
   return it;
@@ -64,13 +71,19 @@ extern "C" int ra_ring_plan(int64_t Sq, int64_t Sk, int P, const ra_layout *layo
     return layout->order == RA_ORDER_RING ? ((r - t) % P + P) % P : (r + t) % P;
   };
 
-  if (kind == RA_LAYOUT_KV_SHARDED) {
+  if (kind == RA_LAYOUT_KV_SHARDED || kind == RA_LAYOUT_KV_SHARDED_CAUSAL) {
     if (Sk % P != 0 || (rank != -1 && rank != 0)) return -1;
+    const bool causal = kind == RA_LAYOUT_KV_SHARDED_CAUSAL;
+    if (causal && Sq > Sk) return -1;
     const int64_t m = Sk / P;
+    const int64_t qpos0 = causal ? Sk - Sq : 0;  // position of query row 0
     for (int t = 0; t < P; ++t) {
       const int s = kv_rank_at(0, t);
       ra_plan_item it = make_item(t, 0, 0, Sq);
-      add_seg(it, s * m, m, 0, s);
+      it.q_pos0 = qpos0;
+      // causal only where the block reaches past the first query's position
+      // (its last key, s*m + m - 1, is after qpos0); earlier blocks are full
+      add_seg(it, s * m, m, causal && s * m + m - 1 > qpos0, s);
       it.first = (t == 0);
       em.emit(it);
     }

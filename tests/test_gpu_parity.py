@@ -290,6 +290,57 @@ def test_kv_sharded_gather_matches_stepwise(dtype):
     assert (l1 - l2).abs().max().item() <= 1e-5
 
 
+KVC_CASES = [
+    # B, Sq, Sk, Hq, Hkv, d, P, dtype
+    (2, 1, 4096, 32, 8, 128, 8, "bf16"),      # decode step: heads packed, sub-blocks gathered
+    (1, 16, 8192, 32, 8, 128, 8, "bf16"),     # 16 draft tokens: causal inside the last block
+    (1, 1000, 8000, 8, 2, 128, 8, "bf16"),    # prefill chunk: 1000-key blocks end mid-tile
+    (1, 300, 1200, 4, 4, 64, 4, "f32"),       # fp32 exact path, d = 64
+]
+
+
+@pytest.mark.parametrize("fuse", [True, False])
+@pytest.mark.parametrize("order", ["ring", "tokenring"])
+@pytest.mark.parametrize("B,Sq,Sk,Hq,Hkv,d,P,dtype", KVC_CASES)
+def test_kv_sharded_causal_matches_oracle(B, Sq, Sk, Hq, Hkv, d, P, dtype, order, fuse):
+    """Queries at the last Sq of Sk positions against K/V cut into P shards,
+    causal on positions, against one-shot causal attention at those positions."""
+    ra = _ra()
+    import torch
+    q, k, v = _inputs(B, Sq, Sk, Hq, Hkv, d, dtype, seed=60 + Sq)
+    out, lse = ra.ring_forward(q, k, v, P, layout="kv_sharded_causal", order=order, fuse_merge=fuse)
+    torch.cuda.synchronize()
+    ro, rl = attention(q.cpu(), k.cpu(), v.cpu(), causal=True, q_pos=np.arange(Sq) + Sk - Sq)
+    compare(f"kv_sharded_causal B{B} Sq{Sq} Sk{Sk} {dtype} {order} fuse={fuse}", out, lse, ro, rl, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("fuse", [True, False])
+def test_kv_sharded_causal_closed_form(dtype, fuse):
+    """Q = 0 makes every visible key score 0, and V's first coordinate holds
+    the key position / 64: query i (position Sk-Sq+i) must get lse = ln(n) and
+    out[..., 0] = (n-1)/128 with n = Sk-Sq+i+1 visible keys -- an off-by-one
+    in the bottom-right mask moves lse by ~1/n and out by 1/128."""
+    ra = _ra()
+    import torch
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    B, Sq, Sk, Hq, Hkv, d, P = 1, 40, 64, 4, 2, 64, 4
+    g = torch.Generator().manual_seed(61)
+    q = torch.zeros(B, Sq, Hq, d)
+    k = torch.randn(B, Sk, Hkv, d, generator=g)
+    v = torch.randn(B, Sk, Hkv, d, generator=g)
+    v[..., 0] = (torch.arange(Sk, dtype=torch.float32) / 64.0)[None, :, None]
+    q, k, v = q.to(tdt).cuda(), k.to(tdt).cuda(), v.to(tdt).cuda()
+    out, lse = ra.ring_forward(q, k, v, P, layout="kv_sharded_causal", fuse_merge=fuse)
+    torch.cuda.synchronize()
+    n = (Sk - Sq + np.arange(Sq) + 1).astype(np.float64)
+    got_lse = lse.double().cpu().numpy()            # [B, Hq, Sq]
+    got0 = out[..., 0].double().cpu().numpy()      # [B, Sq, Hq]
+    assert np.max(np.abs(got_lse - np.log(n)[None, None, :])) <= 1e-5
+    # bf16 rounds P = 1 exactly, so both paths reproduce the mean to fp32 rounding
+    assert np.max(np.abs(got0 - ((n - 1) / 128.0)[None, :, None])) <= 1e-5
+
+
 def test_oracle_ring_emulation_matches_gpu_ring():
     """The oracle's own ring emulation (blockwise) and the GPU agree too."""
     ra = _ra()

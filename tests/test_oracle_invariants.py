@@ -195,6 +195,32 @@ def test_kv_sharded_decode_equals_one_shot():
     assert np.max(np.abs(o - o_ref)) < 1e-12 and np.max(np.abs(l - l_ref)) < 1e-12
 
 
+@pytest.mark.parametrize("Sq,Sk,P", [(1, 24, 4), (6, 24, 3), (24, 24, 4), (10, 40, 8)])
+@pytest.mark.parametrize("order", ["ring", "tokenring"])
+def test_kv_sharded_causal_equals_one_shot(Sq, Sk, P, order):
+    """Blockwise over the K/V shards with the queries at positions
+    Sk-Sq .. Sk-1 equals one-shot causal attention at those positions."""
+    rng = np.random.default_rng(Sq * 100 + Sk + P)
+    q, k, v = _rand(rng, 2, Sq, 4, 8, s=2), _rand(rng, 2, Sk, 2, 8, s=2), _rand(rng, 2, Sk, 2, 8)
+    o_ref, l_ref = attention(q, k, v, causal=True, q_pos=np.arange(Sq) + Sk - Sq)
+    o, l = ring_blockwise(q, k, v, P, layout="kv_sharded_causal", order=order)
+    assert np.max(np.abs(o - o_ref)) < 1e-12 and np.max(np.abs(l - l_ref)) < 1e-12
+
+
+def test_kv_sharded_causal_closed_form_zero_queries():
+    """Q = 0: every visible key has the same score, so query i (position
+    Sk-Sq+i) gets lse = ln(Sk-Sq+i+1) and the mean of V over keys 0..Sk-Sq+i."""
+    rng = np.random.default_rng(5)
+    Sq, Sk, P = 7, 28, 4
+    q = np.zeros((1, Sq, 2, 8))
+    k, v = _rand(rng, 1, Sk, 1, 8), _rand(rng, 1, Sk, 1, 8)
+    o, l = ring_blockwise(q, k, v, P, layout="kv_sharded_causal")
+    for i in range(Sq):
+        n = Sk - Sq + i + 1
+        assert abs(l[0, 0, i] - np.log(n)) < 1e-12
+        assert np.max(np.abs(o[0, i, 1] - v[0, :n, 0].mean(axis=0))) < 1e-12
+
+
 def test_zigzag_balance_closed_form():
     # 2P chunks of c tokens, rank r holds chunks r and 2P-1-r: every rank sees
     # c(c+1)/2 + (r c^2) + ... which sums to 2 P c^2 + c visible pairs.

@@ -120,11 +120,48 @@ def test_kv_sharded_plan():
     assert [it["segs"][0]["kv_rank"] for it in items] == list(range(8))
 
 
+@pytest.mark.parametrize("Sq", [1, 5, 12, 24])
+@pytest.mark.parametrize("P", [1, 2, 3, 4, 8])
+@pytest.mark.parametrize("order", ["ring", "tokenring"])
+def test_kv_sharded_causal_plan(Sq, P, order):
+    """Queries are the last Sq of Sk positions; each visible (query, key) pair
+    with key position <= query position is covered exactly once, a block is
+    flagged causal exactly when some of its keys lie after the first query's
+    position, and block 0 (visible to every query) comes first."""
+    ra = _ra()
+    Sk = 24
+    items = ra.ring_plan(Sq, Sk, P, "kv_sharded_causal", order)
+    assert len(items) == P
+    cnt = np.zeros((Sq, Sk), dtype=np.int64)
+    for it in items:
+        assert it["q_start"] == 0 and it["q_len"] == Sq and it["q_pos0"] == Sk - Sq
+        qpos = it["q_pos0"] + np.arange(Sq)
+        (sg,) = it["segs"]
+        k = np.arange(sg["kv_start"], sg["kv_start"] + sg["kv_len"])
+        assert sg["causal"] == bool(k[-1] > qpos[0])
+        vis = k[None, :] <= qpos[:, None] if sg["causal"] else np.ones((Sq, len(k)), bool)
+        assert vis.any()
+        cnt[:, k] += vis
+    qpos = Sk - Sq + np.arange(Sq)
+    assert np.array_equal(cnt, (np.arange(Sk)[None, :] <= qpos[:, None]).astype(np.int64))
+    assert [it["segs"][0]["kv_rank"] for it in items] == ring_kv_order(0, P, order)
+    assert items[0]["segs"][0]["kv_start"] == 0
+    assert [it["first"] for it in items] == [True] + [False] * (P - 1)
+
+
+def test_q_pos0_is_q_start_for_ring_layouts():
+    ra = _ra()
+    for layout in ("contig", "contig_causal", "zigzag_causal"):
+        assert all(it["q_pos0"] == it["q_start"] for it in ra.ring_plan(48, 48, 4, layout))
+    assert all(it["q_pos0"] == 0 for it in ra.ring_plan(3, 48, 4, "kv_sharded"))
+
+
 @pytest.mark.parametrize("args", [
     (100, 100, 3, "contig"),          # S % P
     (100, 100, 4, "zigzag_causal"),   # S % 2P (100 % 8)
     (64, 32, 4, "contig"),            # Sq != Sk for a ring layout
     (1, 100, 8, "kv_sharded"),        # Sk % P
+    (40, 32, 4, "kv_sharded_causal"), # Sq > Sk: queries must be the last Sq tokens
     (64, 64, 0, "contig"),            # P < 1
     (64, 64, 17, "contig"),           # P > 16
 ])
@@ -140,3 +177,5 @@ def test_plan_rejects_bad_rank():
         ra.ring_plan(64, 64, 4, "contig", rank=4)
     with pytest.raises(ValueError):
         ra.ring_plan(1, 64, 4, "kv_sharded", rank=1)
+    with pytest.raises(ValueError):
+        ra.ring_plan(1, 64, 4, "kv_sharded_causal", rank=1)

@@ -122,6 +122,9 @@ def test_ring_rejects():
     assert _ring(q, k, v, 4, 0, 0, out, lse, ws=FAKE, ws_bytes=100) == RA_E_WORKSPACE
     q2, k2, v2, out2, lse2 = good(Sq=1, Sk=96)
     assert _ring(q2, k2, v2, 4, 0, 1, out2, lse2) == RA_E_INVALID   # Sq != Sk for a ring layout
+    q3, k3, v3, out3, lse3 = good(Sq=96, Sk=64)
+    assert _ring(q3, k3, v3, 4, 4, 1, out3, lse3) == RA_E_INVALID   # causal K/V-sharded: Sq > Sk
+    assert _ring(q3, k3, v3, 4, 5, 1, out3, lse3) == RA_E_INVALID   # no such layout kind
 
 
 def test_workspace_queries():
@@ -143,6 +146,14 @@ def test_workspace_queries():
     kvs = L.RaLayout(3, 0, -1, 1, None, 0)
     n = lib.ra_ring_workspace_bytes(ctypes.byref(q), ctypes.byref(k), 8, ctypes.byref(kvs))
     assert n == 8 * 4 * 16 * 32 * 1 * (128 + 1) * 4
+    # a 4096-token prefill chunk at the end of a 131072-token cache over 8 shards:
+    # 1024 query tiles per block is under two rounds of work-groups, so all 8
+    # blocks' partials are gathered (one partial per block and row)
+    q = T(1, 4096, 32, 128)
+    k = T(1, 131072, 8, 128)
+    kvc = L.RaLayout(4, 0, -1, 1, None, 0)
+    n = lib.ra_ring_workspace_bytes(ctypes.byref(q), ctypes.byref(k), 8, ctypes.byref(kvc))
+    assert n == 8 * 1 * 1 * 32 * 4096 * (128 + 1) * 4
 
 
 def test_merge_rejects():
