@@ -80,6 +80,9 @@ def visible_pairs(w, rank=None):
         return len(list(ranks)) * n * S
     if w.layout == "kv_sharded":
         return w.seq_q * w.seq_k
+    if w.layout == "kv_sharded_causal":
+        # query i sits at position Sk - Sq + i and sees that many keys plus one
+        return w.seq_q * (w.seq_k - w.seq_q) + w.seq_q * (w.seq_q + 1) // 2
     # causal layouts: query at position i sees i+1 keys
     if w.layout == "zigzag_causal":
         c = S // (2 * P)
@@ -104,7 +107,7 @@ def owned_rows(w, rank):
     import numpy as np
 
     S, P = w.seq_q, w.P
-    if rank is None or rank < 0 or w.layout == "kv_sharded":
+    if rank is None or rank < 0 or w.layout.startswith("kv_sharded"):
         return np.arange(S)
     if w.layout == "zigzag_causal":
         c = S // (2 * P)
@@ -143,6 +146,7 @@ def cpu_baseline(w, q, k, v, out=None, lse=None, rank=None, budget_s=12.0):
         threads = os.cpu_count()
     kc, vc = k.cpu(), v.cpu()
     causal = w.layout != "contig" and w.layout != "kv_sharded"
+    q_shift = w.seq_k - w.seq_q if w.layout == "kv_sharded_causal" else 0  # query positions
     S = w.seq_q
     pool = owned_rows(w, rank)
     rng = np.random.default_rng(0)
@@ -153,7 +157,7 @@ def cpu_baseline(w, q, k, v, out=None, lse=None, rank=None, budget_s=12.0):
         sel = np.sort(rng.choice(pool, size=min(rows, len(pool)), replace=False))
         qs = q[:, sel].cpu()
         t0 = time.perf_counter()
-        ro, rl = attention(qs, kc, vc, causal=causal, q_pos=sel)
+        ro, rl = attention(qs, kc, vc, causal=causal, q_pos=sel + q_shift)
         dt = time.perf_counter() - t0
         if out is not None:
             go = out[:, sel].double().cpu().numpy()
@@ -187,7 +191,7 @@ def cpu_baseline(w, q, k, v, out=None, lse=None, rank=None, budget_s=12.0):
         qs = q[:, sel].cpu()
         with threadpool_limits(limits=1):
             t0 = time.perf_counter()
-            attention(qs, kc, vc, causal=causal, q_pos=sel)
+            attention(qs, kc, vc, causal=causal, q_pos=sel + q_shift)
             dt1 = time.perf_counter() - t0
         rec["single_thread"] = {"value": 4.0 * w.head_dim * w.heads_q * w.batch * len(sel) * keys_per_row / dt1 / 1e12,
                                 "unit": "TFLOP/s", "sample": f"{len(sel)} query rows, {dt1:.1f} s"}
@@ -400,8 +404,9 @@ def main():
         "roofline": {
             "bound": roof["bound"],
             "kernel": ("attn_fwd_bf16<%d>" % w.head_dim if w.dtype == "bf16" else "attn_fwd_f32<%d>" % w.head_dim)
-                      + (" (partials for the gather-merge)" if w.layout == "kv_sharded"
-                         else " (fused merge epilogue)" if not args.unfused else ""),
+                      + ("" if args.unfused
+                         else " (partials for the gather-merge)" if w.layout.startswith("kv_sharded")
+                         else " (fused merge epilogue)"),
             "achieved": roof["achieved"],
             "peak": roof["peak"],
             "unit": roof["unit"],

@@ -25,7 +25,7 @@ class Workload:
     seq_q: int
     seq_k: int
     P: int
-    layout: str            # contig | contig_causal | zigzag_causal | kv_sharded
+    layout: str            # contig | contig_causal | zigzag_causal | kv_sharded | kv_sharded_causal
     dtype: str             # "f32" | "bf16"
     std: float
     seed: int
@@ -54,6 +54,10 @@ WORKLOADS = {
     # P=8 blocks of 32768, non-causal.
     "mqa_decode": Workload("mqa_decode", 16, 32, 1, 128, 1, 262144, 8, "kv_sharded",
                            "bf16", 0.5, 5, gen_device="cuda"),
+    # Chunked prefill: the last 4096 tokens of a 131072-token context attend
+    # causally (bottom-right) to K/V in P=8 shards of 16384; GQA 32/8.
+    "prefill_chunk": Workload("prefill_chunk", 1, 32, 8, 128, 4096, 131072, 8, "kv_sharded_causal",
+                              "bf16", 0.5, 6, gen_device="cuda"),
 }
 
 

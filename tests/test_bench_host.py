@@ -49,3 +49,10 @@ def test_contig_owned_rows():
     w = WORKLOADS["mha24k"]
     n = w.seq_q // w.P
     assert np.array_equal(bench.owned_rows(w, 2), np.arange(2 * n, 3 * n))
+
+
+def test_prefill_chunk_pairs_brute_force():
+    w = WORKLOADS["prefill_chunk"]
+    qpos = (w.seq_k - w.seq_q) + np.arange(w.seq_q, dtype=np.int64)
+    assert bench.visible_pairs(w) == int(np.sum(qpos + 1))
+    assert np.array_equal(bench.owned_rows(w, -1), np.arange(w.seq_q))

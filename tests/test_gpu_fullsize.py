@@ -107,6 +107,33 @@ def test_gqa_1m_rank0_share_sampled():
         compare(f"gqa1m rank0 kv{g}", out[:, rows_t][:, :, hs], lse[:, hs][:, :, rows_t], ro, rl, w.dtype)
 
 
+def test_prefill_chunk_sampled():
+    """Chunked prefill at full size: the last 4096 of 131072 tokens, GQA 32/8,
+    K/V in 8 shards (gather-merge path), sampled rows against the oracle."""
+    ra = _ra()
+    import torch
+    w = WORKLOADS["prefill_chunk"]
+    print("[fullsize] prefill_chunk: generating inputs on the GPU", flush=True)
+    q, k, v = make_inputs(w, device="cuda")
+    runner = ra.RingRunner(q, k, v, w.P, layout=w.layout, order=w.order, fuse_merge=True)
+    out, lse = runner.run()
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+    Sq, Sk = w.seq_q, w.seq_k
+    rng = np.random.default_rng(6)
+    rows = np.array(sorted({0, 1, 127, 128, Sq // 2, Sq - 2, Sq - 1} | set(rng.integers(0, Sq, 3).tolist())),
+                    dtype=np.int64)
+    rows_t = torch.as_tensor(rows, device="cuda")
+    group = w.heads_q // w.heads_kv
+    for g in (0, w.heads_kv - 1):
+        hs = slice(g * group, (g + 1) * group)
+        print(f"[fullsize] prefill_chunk: oracle for kv head {g}, {len(rows)} rows", flush=True)
+        qs = q[:, rows_t][:, :, hs].cpu()
+        ro, rl = attention(qs, k[:, :, g:g + 1].cpu(), v[:, :, g:g + 1].cpu(), causal=True,
+                           q_pos=rows + (Sk - Sq))
+        compare(f"prefill_chunk kv{g}", out[:, rows_t][:, :, hs], lse[:, hs][:, :, rows_t], ro, rl, w.dtype)
+
+
 @pytest.mark.parametrize("order,fuse", [("ring", True), ("tokenring", False)])
 def test_mqa_decode_full(order, fuse):
     """MQA decode: B16, 32/1 heads, one query vs 262144 keys over P=8 (all rows)."""
