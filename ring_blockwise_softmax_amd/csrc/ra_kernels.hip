@@ -927,6 +927,77 @@ __global__ __launch_bounds__(kSplitGroups * D / 4) void split_reduce_kernel(cons
   if (d4 == 0) *lp = l;
 }
 
+// Row-parallel form for many rows and few partials (a prefill chunk gathered
+// over the K/V shards): one thread per (row, 4 dims), every partial of its
+// row loaded up front, no cross-thread reduction.  Same combination and
+// same partial order as split_reduce_kernel.
+constexpr int kRowsMaxSplits = 16;
+constexpr int kRowsThreads = 256;
+
+template <int D>
+__global__ __launch_bounds__(kRowsThreads) void split_reduce_rows_kernel(const SplitArgs a) {
+  constexpr int per_row = D / 4;
+  const int64_t nrows = (int64_t)a.B * a.H * a.rows;
+  const int64_t r = (int64_t)blockIdx.x * (kRowsThreads / per_row) + threadIdx.x / per_row;
+  if (r >= nrows) return;
+  const int d4 = threadIdx.x % per_row;
+  const int tok = (int)(r % a.rows);
+  const int h = (int)((r / a.rows) % a.H);
+  const int b = (int)(r / ((int64_t)a.rows * a.H));
+  const int64_t split_stride = nrows;
+
+  float lv[kRowsMaxSplits];
+  f32x4 po[kRowsMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kRowsMaxSplits; ++s) {
+    if (s < a.nsplit) {
+      lv[s] = a.part_lse[r + s * split_stride];
+      po[s] = *(const f32x4 *)(a.part_out + (r + s * split_stride) * D + 4 * d4);
+    }
+  }
+  float m = neg_inf();
+#pragma unroll
+  for (int s = 0; s < kRowsMaxSplits; ++s)
+    if (s < a.nsplit) m = fmaxf(m, lv[s]);
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  float l = neg_inf();
+  if (m != neg_inf()) {
+    float wsum = 0.0f;
+#pragma unroll
+    for (int s = 0; s < kRowsMaxSplits; ++s) {
+      if (s < a.nsplit) {
+        const float w = __expf(lv[s] - m);  // 0 for an empty partial
+        wsum += w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = __builtin_fmaf(w, po[s][e], o[e]);
+      }
+    }
+    const float inv = 1.0f / wsum;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] *= inv;
+    l = m + __logf(wsum);
+  }
+
+  const int orow = a.o_row0 + tok;
+  float *op = a.out + (int64_t)b * a.o_sb + (int64_t)orow * a.o_ss + (int64_t)h * a.o_sh + 4 * d4;
+  float *lp = a.lse + (int64_t)b * a.l_sb + (int64_t)orow * a.l_ss + (int64_t)h * a.l_sh;
+  if (a.mode == kMerge && !a.first) {
+    if (l == neg_inf()) return;
+    const float lr = *lp;
+    if (lr != neg_inf()) {
+      const float diff = l - lr;
+      const float w = 1.0f / (1.0f + __expf(-diff));
+      f32x4 rr = *(const f32x4 *)op;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) rr[j] = rr[j] - w * (rr[j] - o[j]);
+      o = rr;
+      l = fmaxf(lr, l) + log1pf(__expf(-fabsf(diff)));
+    }
+  }
+  *(f32x4 *)op = o;
+  if (d4 == 0) *lp = l;
+}
+
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
@@ -989,6 +1060,15 @@ int launch_merge(const MergeArgs &a, void *stream) {
 int launch_split_reduce(const SplitArgs &a, void *stream) {
   const int64_t rows = (int64_t)a.B * a.H * a.rows;
   if (rows == 0) return 0;
+  if (a.nsplit <= kRowsMaxSplits && rows >= 4096) {  // many rows, few partials
+    const int rows_per_wg = kRowsThreads / (a.D / 4);
+    const dim3 g((unsigned)((rows + rows_per_wg - 1) / rows_per_wg));
+    if (a.D == 128)
+      split_reduce_rows_kernel<128><<<g, dim3(kRowsThreads), 0, (hipStream_t)stream>>>(a);
+    else
+      split_reduce_rows_kernel<64><<<g, dim3(kRowsThreads), 0, (hipStream_t)stream>>>(a);
+    return (int)hipGetLastError();
+  }
   const dim3 grid((unsigned)rows);
   if (a.D == 128)
     split_reduce_kernel<128><<<grid, dim3(kSplitGroups * 32), 0, (hipStream_t)stream>>>(a);

@@ -296,6 +296,7 @@ KVC_CASES = [
     (1, 16, 8192, 32, 8, 128, 8, "bf16"),     # 16 draft tokens: causal inside the last block
     (1, 1000, 8000, 8, 2, 128, 8, "bf16"),    # prefill chunk: 1000-key blocks end mid-tile
     (1, 300, 1200, 4, 4, 64, 4, "f32"),       # fp32 exact path, d = 64
+    (1, 1200, 4800, 4, 4, 64, 4, "bf16"),     # d = 64, 4800 rows x 16 partials: row-parallel reduction
 ]
 
 
