@@ -73,6 +73,11 @@ ra_status check_qkv(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v) 
   if (k->b != q->b || v->b != q->b) return fail(RA_E_INVALID, "batch mismatch");
   if (k->s != v->s || k->h != v->h) return fail(RA_E_INVALID, "k and v shapes differ");
   if (q->h % k->h) return fail(RA_E_INVALID, "Hq (%lld) must be a multiple of Hkv (%lld)", (long long)q->h, (long long)k->h);
+  // Work tiles of one launch are counted in 32 bits: (batch, head, 128-row
+  // tile) triples plus a margin for per-item ragged tiles and key splits.
+  const double tiles = (double)q->b * (double)q->h * ((double)q->s / 128.0 + 1024.0);
+  if (tiles > (double)INT32_MAX)
+    return fail(RA_E_UNSUPPORTED, "B x Hq x Sq too large for one launch's work-tile count");
   return RA_OK;
 }
 

@@ -89,6 +89,22 @@ def test_block_attn_rejects(mutate, status):
     assert _L().lib().ra_last_error()
 
 
+def test_work_tile_count_limit():
+    """B x Hq x Sq beyond a launch's 32-bit work-tile count is refused on the
+    host (the descriptors are never dereferenced, so no memory is needed)."""
+    q, k, v, out, lse = good()
+    for t in (q, k, v, out):
+        t.b = 4096
+    lse.b = 4096
+    for t in (q, out):
+        t.s = 1 << 20
+        t.h = 1024
+    lse.s, lse.h = 1 << 20, 1024
+    k.h = v.h = 1024
+    assert attn(q, k, v, 0, out, lse) == RA_E_UNSUPPORTED
+    assert "work-tile" in _L().lib().ra_last_error().decode()
+
+
 def test_block_attn_rejects_mask():
     q, k, v, out, lse = good()
     assert attn(q, k, v, 3, out, lse) == RA_E_INVALID
