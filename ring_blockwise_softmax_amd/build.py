@@ -26,8 +26,10 @@ COMMON = [
 # Device code: gfx950 only; packed fp32 VALU forms are disabled.
 # -fno-honor-nans: no kernel tests for NaN; without it every fmax pays a
 # NaN-quieting canonicalisation.
+# The iterative ILP scheduler orders the attention stage better than the
+# default occupancy-driven one at the kernel's three-waves-per-SIMD budget.
 DEVICE = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-fno-honor-nans"]
+          "-fno-honor-nans", "-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]
 
 
 def hipcc() -> str:
