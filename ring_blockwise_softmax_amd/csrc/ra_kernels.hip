@@ -1001,30 +1001,26 @@ __global__ __launch_bounds__(kRowsThreads) void split_reduce_rows_kernel(const S
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
+// Dynamic LDS above the default limit must be allowed once per kernel.  The
+// attribute is set by the initialiser of a function-local static, which C++
+// runs exactly once even when several host threads launch concurrently.
 template <typename K>
-static int set_lds(K kernel, size_t bytes, bool &done) {
-  if (!done) {
-    hipError_t e = hipFuncSetAttribute((const void *)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-    if (e != hipSuccess) return (int)e;
-    done = true;
-  }
-  return 0;
+static int allow_lds(K kernel, size_t bytes) {
+  return (int)hipFuncSetAttribute((const void *)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
 template <int D, bool NT>
 static int launch_bf16(const AttnArgs &a, dim3 grid, hipStream_t s) {
-  static bool done = false;
-  const int rc = set_lds(attn_fwd_bf16<D, NT>, Bf16Cfg<D>::LDS_BYTES, done);
-  if (rc) return rc;
+  static const int attr = allow_lds(attn_fwd_bf16<D, NT>, Bf16Cfg<D>::LDS_BYTES);
+  if (attr) return attr;
   attn_fwd_bf16<D, NT><<<grid, dim3(Bf16Cfg<D>::THREADS), Bf16Cfg<D>::LDS_BYTES, s>>>(a);
   return 0;
 }
 
 template <int D>
 static int launch_f32(const AttnArgs &a, dim3 grid, dim3 block, hipStream_t s) {
-  static bool done = false;
-  const int rc = set_lds(attn_fwd_f32<D>, F32Cfg<D>::LDS_BYTES, done);
-  if (rc) return rc;
+  static const int attr = allow_lds(attn_fwd_f32<D>, F32Cfg<D>::LDS_BYTES);
+  if (attr) return attr;
   attn_fwd_f32<D><<<grid, block, F32Cfg<D>::LDS_BYTES, s>>>(a);
   return 0;
 }
