@@ -3,6 +3,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -98,7 +99,7 @@ ra_status check_out(const ra_tensor *q, const ra_tensor *out, const ra_tensor *l
 // ---------------------------------------------------------------------------
 struct Prof {
   std::mutex mu;
-  bool on = false;
+  std::atomic<bool> on{false};  // read without the lock on every launch
   std::vector<hipEvent_t> pool;
   struct Rec {
     int kind;
