@@ -15,6 +15,11 @@ Prints ONE JSON line.  Extra objects:
                    the HBM peak.
   step_ms       -- min / median / max of per-step times (one event pair per
                    step, a separate region from the timed one).
+  clock         -- per-XCD gfx clock (median of the XCD means) and socket
+                   power from the GPU metrics while the same steps run for
+                   ~2 s after the timed regions; roofline.frac_at_sclk is
+                   the kernel against the MFMA peak at that clock (the
+                   nominal peak assumes 2.4 GHz).
   merge         -- the standalone merge kernel at the GQA 1M-token share shape
                    (4,194,304 row-heads x d128, 6.49 GB moved), in GB/s.
   cpu_baseline  -- the fp64 CPU oracle on a bounded sample of the same
@@ -203,6 +208,86 @@ def cpu_baseline(w, q, k, v, out=None, lse=None, rank=None, budget_s=12.0):
     return rec
 
 
+def summarize_clock(samples):
+    """Summary of gfx clock / power samples taken while the GPU was busy.
+
+    samples: list of (per-XCD current gfx clocks in MHz, current socket power
+    in W) tuples; entries that are not numbers ("N/A") are dropped.  The
+    metrics table refreshes slower than it is sampled, so repeated values
+    are kept as they come.
+    """
+    clocks, powers = [], []
+    for xcd, power in samples:
+        vals = [c for c in (xcd or []) if isinstance(c, (int, float))]
+        if vals:
+            clocks.append(sum(vals) / len(vals))
+        if isinstance(power, (int, float)):
+            powers.append(power)
+    if not clocks:
+        return None
+    clocks.sort()
+    out = {"sclk_mhz": round(clocks[len(clocks) // 2], 1),
+           "sclk_mhz_range": [round(clocks[0], 1), round(clocks[-1], 1)],
+           "samples": len(clocks)}
+    if powers:
+        powers.sort()
+        out["socket_power_w"] = powers[len(powers) // 2]
+    return out
+
+
+def clock_telemetry(run_once, seconds=2.0, settle_s=0.5):
+    """Sample the per-XCD gfx clocks and the socket power (amdsmi GPU
+    metrics) while run_once() keeps the GPU busy for `seconds`; the first
+    settle_s are not sampled (the table lags).  None if amdsmi is unusable."""
+    import threading
+
+    import torch
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+    except Exception:
+        return None
+    try:
+        handles = amdsmi.amdsmi_get_processor_handles()
+        h = handles[0] if len(handles) == 1 else None
+        if h is None:
+            bus = getattr(torch.cuda.get_device_properties(0), "pci_bus_id", None)
+            for c in handles:
+                if bus is not None and int(amdsmi.amdsmi_get_gpu_device_bdf(c).split(":")[1], 16) == bus:
+                    h = c
+        if h is None:
+            return None
+        samples, stop = [], threading.Event()
+
+        def sample():
+            time.sleep(settle_s)
+            while not stop.is_set():
+                m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+                samples.append((m.get("current_gfxclks"), m.get("current_socket_power")))
+                stop.wait(0.05)
+
+        th = threading.Thread(target=sample, daemon=True)
+        t0 = time.perf_counter()
+        th.start()
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(5):
+                run_once()
+            torch.cuda.synchronize()
+        stop.set()
+        th.join()
+        res = summarize_clock(samples)
+        if res is not None:
+            res["source"] = "amdsmi GPU metrics, sampled every 50 ms over %.1f s of steps" % (seconds - settle_s)
+        return res
+    except Exception:
+        return None
+    finally:
+        try:
+            amdsmi.amdsmi_shut_down()
+        except Exception:
+            pass
+
+
 def merge_bench(steps=10):
     """Standalone merge at the GQA 1M-token rank-share shape (>= 2 GB)."""
     import torch
@@ -294,6 +379,7 @@ def main():
     ap.add_argument("--rank", type=int, default=None, help="emulate one rank's share only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-merge", action="store_true")
+    ap.add_argument("--no-clock", action="store_true", help="skip the clock / power sampling")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -421,6 +507,13 @@ def main():
         "seed": w.seed,
         "hip": torch.version.hip,
     }
+    # Region 4 (not timed): clocks and power while the same steps run.
+    if not args.no_clock:
+        rec["clock"] = clock_telemetry(runner.run)
+        if rec["clock"] and rec["roofline"]["unit"] == "TFLOP/s":
+            # the same kernel against the MFMA peak at the clock it ran at
+            rec["roofline"]["frac_at_sclk"] = round(
+                roof["achieved"] / (roof["peak"] * rec["clock"]["sclk_mhz"] / 2400.0), 4)
     if args.calib_copy:
         src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)

@@ -56,3 +56,17 @@ def test_prefill_chunk_pairs_brute_force():
     qpos = (w.seq_k - w.seq_q) + np.arange(w.seq_q, dtype=np.int64)
     assert bench.visible_pairs(w) == int(np.sum(qpos + 1))
     assert np.array_equal(bench.owned_rows(w, -1), np.arange(w.seq_q))
+
+
+def test_clock_summary():
+    """Clock / power summary of GPU-metrics samples: the per-XCD clocks are
+    averaged per sample, the median over samples is reported, and "N/A"
+    entries are dropped."""
+    xcd = [1719, 1634, 1691, 1620, 1669, 1631, 1686, 1660]      # MHz, as read on an MI355X
+    s = bench.summarize_clock([(xcd, 1389), (["N/A"] * 8, "N/A"), ([1600] * 8, 1380), ([1700] * 8, 1395)])
+    assert s["sclk_mhz"] == 1663.8                 # median of 1600, 1663.75, 1700
+    assert s["sclk_mhz_range"] == [1600.0, 1700.0]
+    assert s["samples"] == 3
+    assert s["socket_power_w"] == 1389
+    assert bench.summarize_clock([(["N/A"], "N/A")]) is None
+    assert "socket_power_w" not in bench.summarize_clock([([1500], "N/A")])
