@@ -15,6 +15,10 @@ Prints ONE JSON line.  Extra objects:
                    the HBM peak.
   step_ms       -- min / median / max of per-step times (one event pair per
                    step, a separate region from the timed one).
+  roofline.ceiling -- the kernel's matrix instruction alone on random bf16
+                   operands (a probe library), its TFLOP/s, clock and power,
+                   and frac_of_ceiling = achieved / that rate; the same loop
+                   on zero operands runs at full clock for comparison.
   clock         -- per-XCD gfx clock (median of the XCD means) and socket
                    power from the GPU metrics while the same steps run for
                    ~2 s after the timed regions; roofline.frac_at_sclk is
@@ -288,6 +292,53 @@ def clock_telemetry(run_once, seconds=2.0, settle_s=0.5):
             pass
 
 
+def mfma_ceiling(grid=2048, iters=2000):
+    """The attention kernel's matrix instruction alone (libra_probe.so):
+    TFLOP/s of v_mfma_f32_32x32x16_bf16 on random bf16 operands, with the
+    clock and power it ran at, and the same loop on zero operands.  On
+    random data the part cannot sustain its nominal clock, so this is the
+    practical ceiling of a bf16 MFMA kernel on such inputs."""
+    import ctypes
+
+    import torch
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "ring_blockwise_softmax_amd", "libra_probe.so"))
+    g = torch.Generator(device="cuda").manual_seed(1)
+    src = (torch.randn(1024 * 8, device="cuda", generator=g) * 0.5).to(torch.bfloat16)
+    sink = torch.empty(grid * 256, device="cuda")
+    stream = torch.cuda.current_stream()
+    flops = grid * 4 * iters * 8 * 2 * 32 * 32 * 16
+
+    def make(zero):
+        def run():
+            rc = lib.ra_probe_mfma_loop(zero, ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(sink.data_ptr()),
+                                        grid, iters, ctypes.c_void_p(stream.cuda_stream))
+            if rc:
+                raise RuntimeError("MFMA probe launch failed (%d)" % rc)
+        return run
+
+    def rate(run, n=40):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return flops / (e0.elapsed_time(e1) / n / 1e3) / 1e12
+
+    out = {"kind": "v_mfma_f32_32x32x16_bf16 alone, operands cycling through random bf16 registers"}
+    run = make(0)
+    clock = clock_telemetry(run)          # also brings the part to its sustained clock
+    out["tflops"] = round(rate(run), 1)
+    if clock:
+        out["sclk_mhz"], out["socket_power_w"] = clock["sclk_mhz"], clock.get("socket_power_w")
+    zrun = make(1)
+    for _ in range(100):
+        zrun()
+    out["zero_operands_tflops"] = round(rate(zrun), 1)
+    return out
+
+
 def merge_bench(steps=10):
     """Standalone merge at the GQA 1M-token rank-share shape (>= 2 GB)."""
     import torch
@@ -380,6 +431,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-merge", action="store_true")
     ap.add_argument("--no-clock", action="store_true", help="skip the clock / power sampling")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the MFMA-only ceiling measurement")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -514,6 +566,9 @@ def main():
             # the same kernel against the MFMA peak at the clock it ran at
             rec["roofline"]["frac_at_sclk"] = round(
                 roof["achieved"] / (roof["peak"] * rec["clock"]["sclk_mhz"] / 2400.0), 4)
+    if not args.no_ceiling and rec["roofline"]["unit"] == "TFLOP/s" and w.dtype == "bf16":
+        rec["roofline"]["ceiling"] = mfma_ceiling()
+        rec["roofline"]["frac_of_ceiling"] = round(roof["achieved"] / rec["roofline"]["ceiling"]["tflops"], 4)
     if args.calib_copy:
         src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)

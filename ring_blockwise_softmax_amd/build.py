@@ -62,7 +62,25 @@ def build(verbose: bool = False) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    build_probe(cc, verbose)
     return LIB
+
+
+PROBE_LIB = os.path.join(HERE, "libra_probe.so")
+
+
+def build_probe(cc: str, verbose: bool = False) -> str:
+    """The benchmark's MFMA-throughput probe, a library of its own.  Built
+    with the default scheduler: the ILP one places two products on the same
+    accumulator back to back in its loop, which stalls the matrix pipe."""
+    tmp = PROBE_LIB + ".tmp"
+    flags = [f for f in DEVICE if f not in ("-mllvm", "-amdgpu-sched-strategy=iterative-ilp")]
+    cmd = [cc, *COMMON, *flags, "-shared", os.path.join(CSRC, "mfma_ceiling.hip"), "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
 
 
 if __name__ == "__main__":

@@ -182,3 +182,11 @@ def test_merge_rejects():
     assert lib.ra_merge(ctypes.byref(out), ctypes.byref(lse), ctypes.byref(out), ctypes.byref(blse), None) == RA_E_INVALID
     b16 = T(1, 10, 2, 128, 0, data=FAKE + 0x100000)
     assert lib.ra_merge(ctypes.byref(out), ctypes.byref(lse), ctypes.byref(b16), ctypes.byref(blse), None) == RA_E_UNSUPPORTED
+
+
+def test_probe_library_rejects_bad_arguments():
+    """The benchmark's MFMA probe library loads and checks its arguments on
+    the host (nothing is launched)."""
+    lib = ctypes.CDLL(os.path.join(ROOT, "ring_blockwise_softmax_amd", "libra_probe.so"))
+    assert lib.ra_probe_mfma_loop(0, None, None, 0, 1, None) != 0     # no grid
+    assert lib.ra_probe_mfma_loop(0, None, ctypes.c_void_p(FAKE), 8, 1, None) != 0  # operands missing
