@@ -266,7 +266,10 @@ def clock_telemetry(run_once, seconds=2.0, settle_s=0.5):
         def sample():
             time.sleep(settle_s)
             while not stop.is_set():
-                m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+                try:
+                    m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+                except Exception:
+                    return
                 samples.append((m.get("current_gfxclks"), m.get("current_socket_power")))
                 stop.wait(0.05)
 
@@ -302,7 +305,10 @@ def mfma_ceiling(grid=2048, iters=2000):
 
     import torch
 
-    lib = ctypes.CDLL(os.path.join(ROOT, "ring_blockwise_softmax_amd", "libra_probe.so"))
+    try:
+        lib = ctypes.CDLL(os.path.join(ROOT, "ring_blockwise_softmax_amd", "libra_probe.so"))
+    except OSError:
+        return None  # probe library not built
     g = torch.Generator(device="cuda").manual_seed(1)
     src = (torch.randn(1024 * 8, device="cuda", generator=g) * 0.5).to(torch.bfloat16)
     sink = torch.empty(grid * 256, device="cuda")
@@ -567,8 +573,10 @@ def main():
             rec["roofline"]["frac_at_sclk"] = round(
                 roof["achieved"] / (roof["peak"] * rec["clock"]["sclk_mhz"] / 2400.0), 4)
     if not args.no_ceiling and rec["roofline"]["unit"] == "TFLOP/s" and w.dtype == "bf16":
-        rec["roofline"]["ceiling"] = mfma_ceiling()
-        rec["roofline"]["frac_of_ceiling"] = round(roof["achieved"] / rec["roofline"]["ceiling"]["tflops"], 4)
+        ceiling = mfma_ceiling()
+        if ceiling:
+            rec["roofline"]["ceiling"] = ceiling
+            rec["roofline"]["frac_of_ceiling"] = round(roof["achieved"] / ceiling["tflops"], 4)
     if args.calib_copy:
         src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
