@@ -333,10 +333,7 @@ __global__ __launch_bounds__(Bf16Cfg<D>::THREADS, Bf16Cfg<D>::OCC) void attn_fwd
   const int qpos = it.qpos0 + (row_ok ? prow : rows_total - 1) / a.GP;
   const int wave_qpos_min = it.qpos0 + min(wave_row0, rows_total - 1) / a.GP;
   const int tile_qpos_max = it.qpos0 + (min(tile_row0 + C::QT, rows_total) - 1) / a.GP;
-  // On the streamed (decode) shape a tile can hold fewer packed rows than
-  // the work-group: a wave whose 32 rows are all past the item only copies.
-  // (Elsewhere the branch costs more than the rare idle wave saves.)
-  const bool wave_live = !NT || wave_row0 < rows_total;
+  const int wave_qpos_max = it.qpos0 + min(wave_row0 + 31, rows_total - 1) / a.GP;
 
   // Q fragment (B operand of S^T = K Q^T): d = 16*kc + 8*g + 0..7.
   bf16x8 qf[D / 16];
@@ -456,10 +453,6 @@ __global__ __launch_bounds__(Bf16Cfg<D>::THREADS, Bf16Cfg<D>::OCC) void attn_fwd
   // this stage's barrier) is issued, so its address work overlaps the
   // matrix cores.
   auto step = [&](int ti, int bc, bool copy, int bl) {
-    if (!wave_live) {  // no valid row: only the copy share
-      if (copy) issue_next(bl);
-      return;
-    }
     f32x16 s = f32x16{};
 #pragma unroll
     for (int kc = 0; kc < D / 16; ++kc) {
@@ -559,15 +552,46 @@ __global__ __launch_bounds__(Bf16Cfg<D>::THREADS, Bf16Cfg<D>::OCC) void attn_fwd
     }
   };
 
+  // Tiles this wave computes: none if its 32 rows are all past the item (a
+  // ragged last query tile, or fewer packed rows than the work-group); under
+  // a causal last segment, only up to the key of its last row, rounded up to
+  // a whole group of NBUF stages (the extra tiles are fully masked and add
+  // exact zeros).  Past them the wave only does its share of the copies,
+  // with the same waits and barriers, in a second loop; the stage body is not
+  // duplicated and the steady-state loop carries no test.
+  int nt_live = ntiles;
+  if (wave_row0 >= rows_total) {
+    nt_live = 0;
+  } else {
+    const SegRange &sl = it.nseg > 1 ? sr1 : sr0;
+    if (sl.causal) {
+      const int lim = min(sl.hi, wave_qpos_max - sl.kpos0 + 1);
+      const int need = lim <= sl.lo ? 0 : (lim - sl.lo + C::KT - 1) / C::KT;
+      nt_live = (it.nseg > 1 ? nt0 : 0) + min(it.nseg > 1 ? nt1 : nt0, need);
+    }
+  }
+
+  const int nt_main = min(ntiles, (nt_live + C::NBUF - 1) / C::NBUF * C::NBUF);
+
   const int npro = min(ntiles, C::PF);
   for (int j = 0; j < npro; ++j) issue_next(j);
-  for (int ti = 0; ti < ntiles; ti += C::NBUF) {
+  int ti = 0;
+  for (; ti < nt_main; ti += C::NBUF) {
 #pragma unroll
     for (int k = 0; k < C::NBUF; ++k) {
       if (ti + k >= ntiles) break;
       wait_tile(ti + k);
       lds_barrier();
       step(ti + k, k, ti + k + C::PF < ntiles, (k + C::PF) % C::NBUF);
+    }
+  }
+  for (; ti < ntiles; ti += C::NBUF) {  // copies only
+#pragma unroll
+    for (int k = 0; k < C::NBUF; ++k) {
+      if (ti + k >= ntiles) break;
+      wait_tile(ti + k);
+      lds_barrier();
+      if (ti + k + C::PF < ntiles) issue_next((k + C::PF) % C::NBUF);
     }
   }
 
