@@ -102,3 +102,27 @@ def test_merge_into_strided_running_state():
     ro, rl = merge_bshd(o0, l0, bout.double().cpu().numpy(), blse.double().cpu().numpy())
     assert np.abs(out.double().cpu().numpy() - ro).max() <= 1e-5
     assert np.abs(lse.double().cpu().numpy() - rl).max() <= 1e-5
+
+
+def test_mfma_probe_library_runs():
+    """The benchmark's MFMA-only probe (libra_probe.so) runs both operand
+    modes: zero operands give exact zeros; random operands give finite sums."""
+    import ctypes
+    import os
+    import torch
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    lib = ctypes.CDLL(os.path.join(root, "ring_blockwise_softmax_amd", "libra_probe.so"))
+    g = torch.Generator(device="cuda").manual_seed(2)
+    src = (torch.randn(1024 * 8, device="cuda", generator=g) * 0.5).to(torch.bfloat16)
+    grid = 16
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for zero in (1, 0):
+        sink = torch.full((grid * 256,), float("nan"), device="cuda")
+        assert lib.ra_probe_mfma_loop(zero, ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(sink.data_ptr()),
+                                      grid, 4, stream) == 0
+        torch.cuda.synchronize()
+        assert torch.isfinite(sink).all()
+        if zero:
+            assert torch.all(sink == 0)
+        else:
+            assert float(sink.abs().max()) > 0
