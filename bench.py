@@ -212,6 +212,115 @@ def cpu_baseline(w, q, k, v, out=None, lse=None, rank=None, budget_s=12.0):
     return rec
 
 
+def _gpu_ms(run, n=5):
+    """Median time of run() over n event-timed calls after two warm-up calls."""
+    import torch
+
+    for _ in range(2):
+        run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ts = []
+    for _ in range(n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    return sorted(ts)[len(ts) // 2]
+
+
+def oracle_table():
+    """The fp64 oracle timed per configuration beside the GPU (one JSON line
+    each): the tiny ring, the 24k MHA rank-0 share and full ring, the 24k
+    zigzag rank-0 share and the MQA decode step in full; the 1M-token GQA
+    rank-0 share on 64 query rows x 32 heads (chunk edges plus random rows of
+    both of rank 0's chunks), extrapolated to its 131072 rows.  Each line has
+    the oracle's wall time and rate with the threads it used, a single-thread
+    rate on 16 of the same rows (2 for the 1M-token share), the GPU time of the same work and the GPU
+    result's error on the rows the oracle computed."""
+    import numpy as np
+    import torch
+
+    import ring_blockwise_softmax_amd as ra
+    from oracle import attention
+    from ring_blockwise_softmax_amd.workloads import WORKLOADS, make_inputs
+
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [os.cpu_count()])
+    except ImportError:
+        threadpool_limits, threads = None, os.cpu_count()
+
+    def one(name, rank, parts, extrapolate_to=None, label=None, st_rows=16):
+        w = WORKLOADS[name]
+        print(f"[oracle-table] {label or name}: inputs", file=sys.stderr, flush=True)
+        q, k, v = make_inputs(w, device="cuda")
+        runner = ra.RingRunner(q, k, v, w.P, layout=w.layout, order=w.order, rank=rank, fuse_merge=True)
+        gpu_ms = _gpu_ms(runner.run)
+        out, lse = runner.out, runner.lse
+        torch.cuda.synchronize()
+        causal = w.layout not in ("contig", "kv_sharded")
+        q_shift = w.seq_k - w.seq_q if w.layout == "kv_sharded_causal" else 0
+        kc, vc = k.cpu(), v.cpu()
+        t_total, n_rows, eo, el, mo = 0.0, 0, 0.0, 0.0, 0.0
+        for i, rows in enumerate(parts):
+            qs = q[:, torch.as_tensor(rows, device="cuda")].cpu()
+            t0 = time.perf_counter()
+            ro, rl = attention(qs, kc, vc, causal=causal, q_pos=rows + q_shift)
+            dt = time.perf_counter() - t0
+            t_total += dt
+            n_rows += len(rows)
+            rt = torch.as_tensor(rows, device="cuda")
+            go = out[:, rt].double().cpu().numpy()
+            gl = lse[:, :, rt].double().cpu().numpy()
+            eo = max(eo, float(np.max(np.abs(go - ro))))
+            el = max(el, float(np.max(np.abs(gl - rl))))
+            mo = max(mo, float(np.max(np.abs(ro))))
+            print(f"[oracle-table] {label or name}: part {i + 1}/{len(parts)} ({len(rows)} rows) {dt:.1f} s",
+                  file=sys.stderr, flush=True)
+        keys_per_row = visible_pairs(w) / (w.seq_q * 1.0) if causal else w.seq_k
+        if w.layout == "zigzag_causal" and rank is not None and rank >= 0:
+            keys_per_row = visible_pairs(w, rank) / (len(owned_rows(w, rank)) * 1.0)
+        fl = 4.0 * w.head_dim * w.heads_q * w.batch * n_rows * keys_per_row
+        rec = {"config": label or name, "rows_timed": n_rows * w.batch, "heads": w.heads_q,
+               "keys": w.seq_k, "oracle_s": round(t_total, 2), "oracle_tflops": fl / t_total / 1e12,
+               "cores": int(threads), "cpu": cpu_model(), "gpu_ms": round(gpu_ms, 4),
+               "check": {"max_err_out": eo, "max_abs_oracle_out": mo, "max_err_lse": el}}
+        if extrapolate_to:
+            rec["oracle_s_extrapolated"] = round(t_total * extrapolate_to / n_rows, 1)
+            rec["extrapolated_from"] = f"{n_rows} rows x {w.heads_q} heads to {extrapolate_to} rows"
+        rec["speedup_gpu_vs_oracle"] = round(rec.get("oracle_s_extrapolated", t_total) / (gpu_ms / 1e3), 1)
+        if threadpool_limits is not None:
+            sel = parts[0][:st_rows]
+            qs = q[:, torch.as_tensor(sel, device="cuda")].cpu()
+            with threadpool_limits(limits=1):
+                t0 = time.perf_counter()
+                attention(qs, kc, vc, causal=causal, q_pos=sel + q_shift)
+                dt1 = time.perf_counter() - t0
+            rec["single_thread_tflops"] = 4.0 * w.head_dim * w.heads_q * w.batch * len(sel) * keys_per_row / dt1 / 1e12
+        print(json.dumps(rec), flush=True)
+        del q, k, v, kc, vc, runner, out, lse
+        torch.cuda.empty_cache()
+
+    one("tiny", -1, [np.arange(512)])
+    one("mha24k", 0, [np.arange(6000)], label="mha24k rank-0 share")
+    one("mha24k", -1, [np.arange(r * 6000, (r + 1) * 6000) for r in range(4)], label="mha24k full ring")
+    one("zigzag24k", 0, [owned_rows(WORKLOADS["zigzag24k"], 0)], label="zigzag24k rank-0 share")
+    w4 = WORKLOADS["gqa1m"]
+    c = w4.seq_q // (2 * w4.P)
+    hi = (2 * w4.P - 1) * c
+    rng = np.random.default_rng(4)
+    edges = [0, 1, 127, 128, c - 1, hi, hi + 1, hi + 127, hi + 128, w4.seq_q - 1]
+    rest = np.concatenate([rng.choice(np.arange(2, c - 1), 27, replace=False),
+                           rng.choice(np.arange(hi + 2, w4.seq_q - 1), 27, replace=False)])
+    rows4 = np.unique(np.concatenate([edges, rest]))[:64]
+    one("gqa1m", 0, [rows4], extrapolate_to=2 * c, label="gqa1m rank-0 share (sampled)", st_rows=2)
+    one("mqa_decode", -1, [np.arange(1)], label="mqa_decode")
+
+
 def summarize_clock(samples):
     """Summary of gfx clock / power samples taken while the GPU was busy.
 
@@ -440,12 +549,18 @@ def main():
     ap.add_argument("--no-ceiling", action="store_true", help="skip the MFMA-only ceiling measurement")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--oracle-table", action="store_true",
+                    help="only time the CPU oracle per configuration beside the GPU (one JSON line each)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the ring is emulated in one device's memory; "
               "--gpus above 1 is not supported.", file=sys.stderr)
         sys.exit(2)
+
+    if args.oracle_table:
+        oracle_table()
+        return
 
     import torch
 

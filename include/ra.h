@@ -185,6 +185,7 @@ size_t ra_block_attn_workspace_bytes(const ra_tensor *q, const ra_tensor *k);
 /* ra_merge -- fold a partial into the running pair, in place (TokenRing
  * review, "What carries the argument"; paper section 3.1).
  *   out, block_out: [B, S, H, d] fp32;  lse, block_lse: [B, S, H] fp32 (d = 1).
+ *   d is one of 4, 8, 16, 32, 64, 128, 256 (else RA_E_UNSUPPORTED).
  * out/lse are read and overwritten; block_* are read.  An lse of -inf is the
  * identity on either side.  out must not alias block_out. */
 ra_status ra_merge(ra_tensor *out, ra_tensor *lse, const ra_tensor *block_out,

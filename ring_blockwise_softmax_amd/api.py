@@ -35,6 +35,22 @@ def _workspace(nbytes, device):
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
+def _used_on(stream, *tensors):
+    """Mark tensors allocated on torch's current stream as used by ``stream``.
+
+    The kernels run on ``stream``; when that is not the current stream, the
+    caching allocator must not hand these blocks to other work (e.g. after a
+    temporary workspace is freed on return) before ``stream`` has finished.
+    """
+    import torch
+
+    if stream is None or stream == torch.cuda.current_stream():
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
+
+
 def block_attn_workspace_bytes(q, k) -> int:
     tq, tk = L.bshd(q), L.bshd(k)
     return int(L.lib().ra_block_attn_workspace_bytes(ctypes.byref(tq), ctypes.byref(tk)))
@@ -53,6 +69,7 @@ def block_attn_fwd(q, k, v, mask="none", out=None, lse=None, workspace=None, str
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     L.check(lib.ra_block_attn_fwd(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), L.MASKS[mask],
                                   ctypes.byref(to), ctypes.byref(tl), wptr, wbytes, L.stream_ptr(stream)))
+    _used_on(stream, out, lse, workspace)
     return out, lse
 
 
@@ -105,6 +122,7 @@ class RingRunner:
         L.check(self.lib.ra_ring_forward(ctypes.byref(self.tq), ctypes.byref(self.tk), ctypes.byref(self.tv),
                                          self.P, ctypes.byref(self.lay), ctypes.byref(self.to),
                                          ctypes.byref(self.tl), L.stream_ptr(stream)))
+        _used_on(stream, self.out, self.lse, self.workspace)
         return self.out, self.lse
 
 

@@ -439,7 +439,12 @@ ra_status ra_merge(ra_tensor *out, ra_tensor *lse, const ra_tensor *bout, const 
       (st = check_tensor(bout, "block_out", false)) || (st = check_tensor(blse, "block_lse", true)))
     return st;
   if (out->dtype != RA_F32 || bout->dtype != RA_F32) return fail(RA_E_UNSUPPORTED, "merge operands must be fp32");
-  if (out->d % 4) return fail(RA_E_UNSUPPORTED, "head_dim must be a multiple of 4");
+  // One thread per 4 dims; the thread of dims 0..3 writes the new lse after
+  // every thread of its row has read the old one.  That order holds only when
+  // a row's threads sit in one wave, i.e. when d/4 divides the wave size.
+  if (out->d % 4 || 64 % (out->d / 4))
+    return fail(RA_E_UNSUPPORTED, "merge head_dim %lld not supported (4, 8, 16, 32, 64, 128 or 256)",
+                (long long)out->d);
   if (bout->b != out->b || bout->s != out->s || bout->h != out->h || bout->d != out->d)
     return fail(RA_E_INVALID, "block_out shape differs from out");
   if (lse->b != out->b || lse->s != out->s || lse->h != out->h || blse->b != out->b || blse->s != out->s ||

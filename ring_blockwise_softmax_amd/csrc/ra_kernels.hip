@@ -71,21 +71,21 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "me
 // track these copies and wait for them before unrelated LDS reads; the
 // kernels wait for them explicitly (s_waitcnt vmcnt) before publishing a
 // tile.  No register outputs; the addresses are consumed at issue.  The LDS
-// destination is taken from M0, which the asm sets (one wait state before
-// the copy reads it) and declares clobbered; nothing else in these kernels
-// keeps a value in M0 (gfx950 LDS instructions do not use it).
+// destination is read from M0, which is bound as an input operand ("{m0}"),
+// so the compiler itself loads M0 and knows it is live up to the copy; the
+// s_nop is the one wait state an M0 write needs before an LDS DMA reads it.
 template <bool NT>
 __device__ __forceinline__ void copy16_to_lds(const void *sbase, uint32_t voff, uint32_t lds_addr) {
   if constexpr (NT)
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
                  :
-                 : "v"(voff), "s"(sbase), "s"(lds_addr)
-                 : "memory", "m0");
+                 : "v"(voff), "s"(sbase), "{m0}"(lds_addr)
+                 : "memory");
   else
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                  :
-                 : "v"(voff), "s"(sbase), "s"(lds_addr)
-                 : "memory", "m0");
+                 : "v"(voff), "s"(sbase), "{m0}"(lds_addr)
+                 : "memory");
 }
 
 // max / sum of a value with its partner lane in the other half of the wave.

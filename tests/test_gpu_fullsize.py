@@ -49,62 +49,114 @@ def test_tiny_config_full(order, fuse):
     compare(f"tiny {order} fuse={fuse}", out, lse, ro, rl, "f32")
 
 
+_INPUTS = {}
+
+
+def _cached_inputs(w):
+    """The 24k inputs are drawn on the CPU (seconds); share them between the
+    variants of one workload."""
+    key = (w.name, w.dtype, w.std, w.heads_q)
+    if key not in _INPUTS:
+        _INPUTS.clear()
+        print(f"[fullsize] {w.name}: generating inputs", flush=True)
+        _INPUTS[key] = make_inputs(w, device="cuda")
+    return _INPUTS[key]
+
+
+@pytest.mark.parametrize("order,fuse", [("ring", True), ("tokenring", True), ("ring", False)])
 @pytest.mark.parametrize("name", ["mha24k", "zigzag24k"])
-def test_24k_configs_sampled(name):
+def test_24k_configs_sampled(name, order, fuse):
     ra = _ra()
     import torch
     w = WORKLOADS[name]
-    print(f"[fullsize] {name}: generating inputs", flush=True)
-    q, k, v = make_inputs(w, device="cuda")
-    runner = ra.RingRunner(q, k, v, w.P, layout=w.layout, order=w.order, rank=w.rank, fuse_merge=True)
+    q, k, v = _cached_inputs(w)
+    runner = ra.RingRunner(q, k, v, w.P, layout=w.layout, order=order, rank=w.rank, fuse_merge=fuse)
     out, lse = runner.run()
     torch.cuda.synchronize()
     nb = 2 * w.P if w.layout == "zigzag_causal" else w.P
     rows = _sample_rows(w.seq_q, _block_edges(w.seq_q, nb), 24, seed=w.seed)
-    print(f"[fullsize] {name}: oracle on {len(rows)} rows x {w.heads_q} heads", flush=True)
+    print(f"[fullsize] {name} {order} fuse={fuse}: oracle on {len(rows)} rows x {w.heads_q} heads", flush=True)
     ro, rl = attention(q.cpu(), k.cpu(), v.cpu(), causal=(w.layout != "contig"), rows=rows)
     rows_t = torch.as_tensor(rows, device="cuda")
-    compare(f"{name} sampled", out[:, rows_t], lse[:, :, rows_t], ro, rl, w.dtype)
+    compare(f"{name} {order} fuse={fuse} sampled", out[:, rows_t], lse[:, :, rows_t], ro, rl, w.dtype)
     # the whole output must be finite and lse within the attainable range
     assert torch.isfinite(out).all() and torch.isfinite(lse).all()
 
 
-def test_gqa_1m_rank0_share_sampled():
-    """GQA 32/8, 1,048,576 tokens over P=8, zigzag; rank 0's share only."""
+# The medium fp32 configuration: the 24k sequence over a 4-rank ring with 4
+# heads, fp32 N(0,1) inputs (the tiny configuration's distribution), so every
+# block is a 6000-key loop ending in a 16-key ragged tile (6000 = 187*32 + 16)
+# and the fp32 kernel's lazy rescale runs the length of the real blocks.
+MEDIUM_F32 = WORKLOADS["mha24k"].with_(name="medium_f32", heads_q=4, heads_kv=4, dtype="f32", std=1.0, seed=7)
+
+
+@pytest.mark.parametrize("layout,order,fuse", [
+    ("contig", "ring", True),
+    ("contig", "ring", False),
+    ("contig", "tokenring", True),
+    ("zigzag_causal", "ring", True),
+    ("zigzag_causal", "tokenring", False),
+])
+def test_medium_f32_sampled(layout, order, fuse):
+    """fp32 at H=4, S=24000, P=4 against the oracle on >= 256 sampled rows,
+    including every block's first/last rows and rows 127/128 of its tiles."""
+    ra = _ra()
+    import torch
+    w = MEDIUM_F32.with_(layout=layout)
+    q, k, v = _cached_inputs(w)
+    out, lse = ra.ring_forward(q, k, v, w.P, layout=layout, order=order, fuse_merge=fuse)
+    torch.cuda.synchronize()
+    nb = 2 * w.P if layout == "zigzag_causal" else w.P
+    rows = _sample_rows(w.seq_q, _block_edges(w.seq_q, nb), 256, seed=w.seed)
+    assert len(rows) >= 256
+    print(f"[fullsize] medium f32 {layout} {order} fuse={fuse}: oracle on {len(rows)} rows", flush=True)
+    ro, rl = attention(q.cpu(), k.cpu(), v.cpu(), causal=(layout != "contig"), rows=rows)
+    rows_t = torch.as_tensor(rows, device="cuda")
+    compare(f"medium f32 {layout} {order} fuse={fuse}", out[:, rows_t], lse[:, :, rows_t], ro, rl, "f32")
+    assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+
+
+@pytest.mark.parametrize("rank,kv_heads", [(0, (0, 7)), (7, (0, 2, 5, 7))])
+def test_gqa_1m_rank_share_sampled(rank, kv_heads):
+    """GQA 32/8, 1,048,576 tokens over P=8, zigzag; one rank's share only.
+    Rank 0 owns chunks 0 and 15, rank 7 chunks 7 and 8 (the middle of the
+    sequence, the other end of every owner's merge schedule)."""
     ra = _ra()
     import torch
     w = WORKLOADS["gqa1m"]
-    print("[fullsize] gqa1m: generating inputs on the GPU", flush=True)
+    print(f"[fullsize] gqa1m rank {rank}: generating inputs on the GPU", flush=True)
     q, k, v = make_inputs(w, device="cuda")
     S, P = w.seq_q, w.P
     c = S // (2 * P)
+    lo, hi = rank * c, (2 * P - 1 - rank) * c   # first rows of the two owned chunks
     out = torch.full((1, S, w.heads_q, w.head_dim), float("nan"), device="cuda")
     lse = torch.full((1, w.heads_q, S), float("nan"), device="cuda")
-    runner = ra.RingRunner(q, k, v, P, layout=w.layout, order=w.order, rank=0, fuse_merge=True,
+    runner = ra.RingRunner(q, k, v, P, layout=w.layout, order=w.order, rank=rank, fuse_merge=True,
                            out=out, lse=lse)
-    print("[fullsize] gqa1m: running rank 0's share", flush=True)
+    print(f"[fullsize] gqa1m: running rank {rank}'s share", flush=True)
     runner.run()
     torch.cuda.synchronize()
     print("[fullsize] gqa1m: done on GPU, checking", flush=True)
-    # rank 0 owns chunks 0 and 2P-1; its rows must all be written (finite)
-    own = torch.cat([out[:, :c], out[:, (2 * P - 1) * c:]], dim=1)
+    # the rank's two chunks must all be written (finite), others untouched
+    own = torch.cat([out[:, lo:lo + c], out[:, hi:hi + c]], dim=1)
     assert torch.isfinite(own).all()
-    assert torch.isnan(out[:, c:c + 1000]).all(), "rows of other ranks were written"
-    edges = [0, 1, 127, 128, c - 1, (2 * P - 1) * c, (2 * P - 1) * c + 1, S - 129, S - 1]
-    rng = np.random.default_rng(4)
-    rows = sorted(set(edges) | set(rng.integers(0, c, 3).tolist()) |
-                  set(((2 * P - 1) * c + rng.integers(0, c, 3)).tolist()))
+    other = (rank + 1) * c if rank + 1 < 2 * P - 1 - rank else 0
+    assert torch.isnan(out[:, other:other + 1000]).all(), "rows of other ranks were written"
+    edges = [lo, lo + 1, lo + 127, lo + 128, lo + c - 1, hi, hi + 1, hi + c - 129, hi + c - 1]
+    rng = np.random.default_rng(4 + rank)
+    rows = sorted(set(edges) | set((lo + rng.integers(0, c, 3)).tolist()) |
+                  set((hi + rng.integers(0, c, 3)).tolist()))
     rows = np.array(rows, dtype=np.int64)
     rows_t = torch.as_tensor(rows, device="cuda")
     group = w.heads_q // w.heads_kv
-    for g in (0, w.heads_kv - 1):            # two K/V heads -> 8 query heads
+    for g in kv_heads:                       # each K/V head -> 4 query heads
         hs = slice(g * group, (g + 1) * group)
-        print(f"[fullsize] gqa1m: oracle for kv head {g}, {len(rows)} rows", flush=True)
+        print(f"[fullsize] gqa1m rank {rank}: oracle for kv head {g}, {len(rows)} rows", flush=True)
         qs = q[:, rows_t][:, :, hs].cpu()
         kk = k[:, :, g:g + 1].cpu()
         vv = v[:, :, g:g + 1].cpu()
         ro, rl = attention(qs, kk, vv, causal=True, q_pos=rows)
-        compare(f"gqa1m rank0 kv{g}", out[:, rows_t][:, :, hs], lse[:, hs][:, :, rows_t], ro, rl, w.dtype)
+        compare(f"gqa1m rank{rank} kv{g}", out[:, rows_t][:, :, hs], lse[:, hs][:, :, rows_t], ro, rl, w.dtype)
 
 
 def test_prefill_chunk_sampled():

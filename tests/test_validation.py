@@ -184,9 +184,23 @@ def test_merge_rejects():
     assert lib.ra_merge(ctypes.byref(out), ctypes.byref(lse), ctypes.byref(b16), ctypes.byref(blse), None) == RA_E_UNSUPPORTED
 
 
+@pytest.mark.parametrize("d", [12, 96, 192, 512])
+def test_merge_rejects_head_dims_that_split_a_row_over_waves(d):
+    """A row's d/4 threads must sit in one wave (the lse is rewritten by one of
+    them after all have read it), so d/4 must divide 64."""
+    L = _L()
+    lib = L.lib()
+    out, bout = T(1, 10, 2, d, 1), T(1, 10, 2, d, 1, data=FAKE + 0x100000)
+    lse, blse = LSE(1, 10, 2), LSE(1, 10, 2, data=FAKE + 0x200000)
+    st = lib.ra_merge(ctypes.byref(out), ctypes.byref(lse), ctypes.byref(bout), ctypes.byref(blse), None)
+    assert st == RA_E_UNSUPPORTED
+    assert b"head_dim" in lib.ra_last_error()
+
+
 def test_probe_library_rejects_bad_arguments():
     """The benchmark's MFMA probe library loads and checks its arguments on
     the host (nothing is launched)."""
     lib = ctypes.CDLL(os.path.join(ROOT, "ring_blockwise_softmax_amd", "libra_probe.so"))
     assert lib.ra_probe_mfma_loop(0, None, None, 0, 1, None) != 0     # no grid
     assert lib.ra_probe_mfma_loop(0, None, ctypes.c_void_p(FAKE), 8, 1, None) != 0  # operands missing
+
