@@ -182,6 +182,30 @@ ra_status ra_block_attn_fwd(const ra_tensor *q, const ra_tensor *k, const ra_ten
 
 size_t ra_block_attn_workspace_bytes(const ra_tensor *q, const ra_tensor *k);
 
+/* ra_block_attn_fwd_noalloc -- ra_block_attn_fwd for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, same kernels and same
+ * results as ra_block_attn_fwd with a workspace of
+ * ra_block_attn_workspace_bytes(q, k) bytes, but the split-K partials live in
+ * a static device array of RA_NOALLOC_SCRATCH_BYTES held by the library: one
+ * copy per GPU, allocated when the code object is loaded and kept until the
+ * process ends.  No call allocates or frees memory.
+ *   - A block whose split partials need more than RA_NOALLOC_SCRATCH_BYTES
+ *     (ra_block_attn_workspace_bytes > the limit) is rejected with
+ *     RA_E_UNSUPPORTED before anything is enqueued.
+ *   - Every call on one GPU shares that GPU's array: calls that overlap in
+ *     time on one GPU (two streams, two host threads) race and give wrong
+ *     results.  Calls in one stream are ordered and safe.  The array keeps the
+ *     last call's partials; nothing in it needs to start at zero (every
+ *     partial is written before it is read).
+ *   - The first call on a device (with that device current) looks up the
+ *     array's device address; a failure there is RA_E_HIP. */
+#define RA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+ra_status ra_block_attn_fwd_noalloc(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v,
+                                    int causal_mask_kind, ra_tensor *out, ra_tensor *lse,
+                                    void *stream);
+
 /* ra_merge -- fold a partial into the running pair, in place (TokenRing
  * review, "What carries the argument"; paper section 3.1).
  *   out, block_out: [B, S, H, d] fp32;  lse, block_lse: [B, S, H] fp32 (d = 1).

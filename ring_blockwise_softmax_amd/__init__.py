@@ -12,6 +12,7 @@ library; the first call does, and fails loudly if it is missing.
 
 from .api import (  # noqa: F401
     block_attn_fwd,
+    block_attn_fwd_noalloc,
     block_attn_workspace_bytes,
     merge,
     ring_forward,

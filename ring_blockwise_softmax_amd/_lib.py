@@ -22,6 +22,8 @@ MASKS = {"none": 0, "causal": 1, "causal_bottom_right": 2}
 LAYOUTS = {"contig": 0, "contig_causal": 1, "zigzag_causal": 2, "kv_sharded": 3, "kv_sharded_causal": 4}
 ORDERS = {"ring": 0, "tokenring": 1}
 KERNEL_KINDS = ("attn", "merge", "split_reduce")
+# Size of the static device scratch of ra_block_attn_fwd_noalloc (RA_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class RaTensor(ctypes.Structure):
@@ -51,6 +53,8 @@ EXPORTS = {
     "ra_block_attn_fwd": (ctypes.c_int, [ctypes.POINTER(RaTensor)] * 3 + [ctypes.c_int] +
                           [ctypes.POINTER(RaTensor)] * 2 + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "ra_block_attn_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(RaTensor)] * 2),
+    "ra_block_attn_fwd_noalloc": (ctypes.c_int, [ctypes.POINTER(RaTensor)] * 3 + [ctypes.c_int] +
+                                  [ctypes.POINTER(RaTensor)] * 2 + [ctypes.c_void_p]),
     "ra_merge": (ctypes.c_int, [ctypes.POINTER(RaTensor)] * 4 + [ctypes.c_void_p]),
     "ra_ring_forward": (ctypes.c_int, [ctypes.POINTER(RaTensor)] * 3 + [ctypes.c_int, ctypes.POINTER(RaLayout)] +
                         [ctypes.POINTER(RaTensor)] * 2 + [ctypes.c_void_p]),

@@ -1,6 +1,7 @@
 """Python entry points with the C ABI's names (marshalling only).
 
 block_attn_fwd  -- one query block against one K/V block -> (block_out, block_lse)
+block_attn_fwd_noalloc -- the same into caller-provided outputs, no allocation
 merge           -- fold a partial into the running (out, lse), in place
 ring_forward    -- the emulated P-step ring (Ring Attention / TokenRing order,
                    contiguous or zigzag causal partition)
@@ -70,6 +71,18 @@ def block_attn_fwd(q, k, v, mask="none", out=None, lse=None, workspace=None, str
     L.check(lib.ra_block_attn_fwd(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), L.MASKS[mask],
                                   ctypes.byref(to), ctypes.byref(tl), wptr, wbytes, L.stream_ptr(stream)))
     _used_on(stream, out, lse, workspace)
+    return out, lse
+
+
+def block_attn_fwd_noalloc(q, k, v, out, lse, mask="none", stream=None):
+    """block_attn_fwd into caller-provided out/lse with no allocation at all:
+    split-K partials use the library's static device scratch (calls that
+    overlap in time on one GPU race; calls in one stream are ordered)."""
+    lib = L.lib()
+    tq, tk, tv = L.bshd(q), L.bshd(k), L.bshd(v)
+    to, tl = L.bshd(out), L.lse_desc(lse)
+    L.check(lib.ra_block_attn_fwd_noalloc(ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), L.MASKS[mask],
+                                          ctypes.byref(to), ctypes.byref(tl), L.stream_ptr(stream)))
     return out, lse
 
 

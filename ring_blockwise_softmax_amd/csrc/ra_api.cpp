@@ -401,16 +401,24 @@ size_t ra_block_attn_workspace_bytes(const ra_tensor *q, const ra_tensor *k) {
   return single_item_ws(q->dtype, q->b, q->h, GP, q->s, k->s, q->d);
 }
 
-ra_status ra_block_attn_fwd(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v, int mask,
-                            ra_tensor *out, ra_tensor *lse, void *workspace, size_t workspace_bytes,
-                            void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Host-side checks of a block call (no HIP call).
+ra_status check_block(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v, int mask, const ra_tensor *out,
+                      const ra_tensor *lse) {
   ra_status st;
   if ((st = check_qkv(q, k, v)) || (st = check_out(q, out, lse, "out", "lse"))) return st;
   if (mask < RA_MASK_NONE || mask > RA_MASK_CAUSAL_BOTTOM_RIGHT) return fail(RA_E_INVALID, "unknown mask kind %d", mask);
   if (mask == RA_MASK_CAUSAL_BOTTOM_RIGHT && q->s > k->s)
     return fail(RA_E_INVALID, "bottom-right causal mask needs Sq <= Sk");
-  if (q->s == 0 || q->b == 0) return RA_OK;
+  return RA_OK;
+}
 
+// One query block against one K/V block (arguments already checked).
+ra_status block_attn(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v, int mask, ra_tensor *out,
+                     ra_tensor *lse, void *workspace, size_t workspace_bytes, void *stream) {
   AttnArgs a{};
   fill_strides(a, q, k, v);
   set_dest(a, (float *)out->data, out->sb, out->ss, out->sh, (float *)lse->data, lse->sb, lse->ss, lse->sh);
@@ -431,6 +439,36 @@ ra_status ra_block_attn_fwd(const ra_tensor *q, const ra_tensor *k, const ra_ten
   it.seg[0].kpos0 = 0;
   it.seg[0].causal = mask != RA_MASK_NONE;
   return run_single_item(a, q->dtype, (int)q->d, (char *)workspace, workspace_bytes, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+ra_status ra_block_attn_fwd(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v, int mask,
+                            ra_tensor *out, ra_tensor *lse, void *workspace, size_t workspace_bytes,
+                            void *stream) {
+  ra_status st;
+  if ((st = check_block(q, k, v, mask, out, lse))) return st;
+  if (q->s == 0 || q->b == 0) return RA_OK;
+  return block_attn(q, k, v, mask, out, lse, workspace, workspace_bytes, stream);
+}
+
+ra_status ra_block_attn_fwd_noalloc(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v, int mask,
+                                    ra_tensor *out, ra_tensor *lse, void *stream) {
+  ra_status st;
+  if ((st = check_block(q, k, v, mask, out, lse))) return st;
+  // The split partials this block would use (0 when the keys are not split).
+  const size_t need = ra_block_attn_workspace_bytes(q, k);
+  if (need > RA_NOALLOC_SCRATCH_BYTES)
+    return fail(RA_E_UNSUPPORTED, "split-K partials of %zu bytes exceed the static scratch of %zu bytes", need,
+                (size_t)RA_NOALLOC_SCRATCH_BYTES);
+  if (q->s == 0 || q->b == 0) return RA_OK;
+  void *ws = nullptr;
+  size_t ws_bytes = 0;
+  const int rc = noalloc_scratch(&ws, &ws_bytes);
+  if (rc) return hip_fail(rc, "static scratch address");
+  return block_attn(q, k, v, mask, out, lse, ws, ws_bytes, stream);
 }
 
 ra_status ra_merge(ra_tensor *out, ra_tensor *lse, const ra_tensor *bout, const ra_tensor *blse, void *stream) {

@@ -4,6 +4,7 @@
 // plan buffer is ever allocated.
 #pragma once
 
+#include <stddef.h>
 #include <stdint.h>
 
 namespace ra {
@@ -96,6 +97,10 @@ struct SplitArgs {
 int launch_attn(const AttnArgs &a, int dtype, int head_dim, void *stream);
 int launch_merge(const MergeArgs &a, void *stream);
 int launch_split_reduce(const SplitArgs &a, void *stream);
+
+// Device address of the static scratch array on the current device (looked
+// up once per device) and its size in bytes.  Returns a hipError_t as int.
+int noalloc_scratch(void **ptr, size_t *bytes);
 
 // Tile geometry the host needs for planning.
 constexpr int kQTileF32 = 128;   // packed query rows per work-group (fp32 kernel)

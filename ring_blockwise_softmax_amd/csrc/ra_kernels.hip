@@ -36,6 +36,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
+#include "ra.h"
 #include "ra_internal.h"
 
 namespace ra {
@@ -1020,6 +1023,36 @@ __global__ __launch_bounds__(kRowsThreads) void split_reduce_rows_kernel(const S
   }
   *(f32x4 *)op = o;
   if (d4 == 0) *lp = l;
+}
+
+// ---------------------------------------------------------------------------
+// Static scratch of the entry point that allocates nothing.  Each GPU holds
+// its own copy from code-object load to process end.  Host code never uses
+// the array's name as an address (on the host it is only a stand-in symbol):
+// the device address is looked up once per device and passed to kernels.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[RA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+
+int noalloc_scratch(void **ptr, size_t *bytes) {
+  static std::mutex mu;
+  static void *addr[kMaxScratchDevices] = {};
+  int dev = 0;
+  hipError_t rc = hipGetDevice(&dev);
+  if (rc != hipSuccess) return (int)rc;
+  if (dev < 0 || dev >= kMaxScratchDevices) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (addr[dev] == nullptr) {
+    void *p = nullptr;
+    rc = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (rc != hipSuccess) return (int)rc;
+    if (p == nullptr) return (int)hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  *bytes = sizeof(scratch);
+  return 0;
 }
 
 // ---------------------------------------------------------------------------

@@ -204,3 +204,28 @@ def test_probe_library_rejects_bad_arguments():
     assert lib.ra_probe_mfma_loop(0, None, None, 0, 1, None) != 0     # no grid
     assert lib.ra_probe_mfma_loop(0, None, ctypes.c_void_p(FAKE), 8, 1, None) != 0  # operands missing
 
+
+def test_noalloc_rejects_before_any_hip_call():
+    """The no-allocation entry point checks its arguments and the size of the
+    split partials it would need on the host: bad arguments and blocks whose
+    partials exceed the static scratch are rejected with nothing enqueued."""
+    L = _L()
+    lib = L.lib()
+
+    def call(q, k, v, mask, o, l):
+        return lib.ra_block_attn_fwd_noalloc(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), mask,
+                                             ctypes.byref(o), ctypes.byref(l), None)
+
+    q, k, v, o, l = good()
+    q.dtype = 7
+    assert call(q, k, v, 0, o, l) == RA_E_UNSUPPORTED
+    q, k, v, o, l = good()
+    assert call(q, k, v, 9, o, l) == RA_E_INVALID
+    # B1 Hq32/Hkv1 Sq4 against 32768 keys: 4 x 32 packed rows in one tile, so
+    # the keys are split 512 ways: 512 * 32 * 4 * (128 + 1) * 4 bytes of
+    # partials, just over the 32 MiB scratch.
+    q, k, v, o, l = good(Sq=4, Sk=32768, Hq=32, Hkv=1)
+    need = lib.ra_block_attn_workspace_bytes(ctypes.byref(q), ctypes.byref(k))
+    assert need == 512 * 32 * 4 * 129 * 4 > L.NOALLOC_SCRATCH_BYTES
+    assert call(q, k, v, 0, o, l) == RA_E_UNSUPPORTED
+    assert b"static scratch" in lib.ra_last_error()
