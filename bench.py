@@ -321,6 +321,45 @@ def oracle_table():
     one("mqa_decode", -1, [np.arange(1)], label="mqa_decode")
 
 
+def traffic_probe():
+    """A fixed sequence of launches for per-dispatch counter runs (rocprofv3
+    --pmc): a 1 GiB device copy (counter calibration); twice a write-only
+    block launch of the 24k step's shape (B4 H32, 6000 x 6000: K/V re-read by
+    47 query tiles); twice the same keys against 128 query rows (K/V read by
+    a single work-group); one fused mha24k ring (step 0 writes, steps 1-3
+    merge); one unfused ring (attention into the workspace plus the merge
+    kernel).  Nothing is timed; the dispatch order is the record."""
+    import torch
+
+    import ring_blockwise_softmax_amd as ra
+    from ring_blockwise_softmax_amd.workloads import Workload, WORKLOADS, make_inputs
+
+    src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    w = Workload("blk", 4, 32, 32, 128, 6000, 6000, 1, "contig", "bf16", 0.5, 9)
+    q, k, v = make_inputs(w, device="cuda")
+    out = torch.empty(4, 6000, 32, 128, device="cuda")
+    lse = torch.empty(4, 32, 6000, device="cuda")
+    for _ in range(2):
+        ra.block_attn_fwd(q, k, v, out=out, lse=lse)
+        torch.cuda.synchronize()
+    q2, o2, l2 = q[:, :128].contiguous(), out[:, :128].contiguous(), lse[:, :, :128].contiguous()
+    for _ in range(2):
+        ra.block_attn_fwd(q2, k, v, out=o2, lse=l2)
+        torch.cuda.synchronize()
+    del q, k, v, out, lse, q2, o2, l2
+    wm = WORKLOADS["mha24k"]
+    q, k, v = make_inputs(wm, device="cuda")
+    ra.RingRunner(q, k, v, wm.P, layout=wm.layout, fuse_merge=True).run()
+    torch.cuda.synchronize()
+    ra.RingRunner(q, k, v, wm.P, layout=wm.layout, fuse_merge=False).run()
+    torch.cuda.synchronize()
+
+
 def summarize_clock(samples):
     """Summary of gfx clock / power samples taken while the GPU was busy.
 
@@ -551,6 +590,8 @@ def main():
                     help="also run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--oracle-table", action="store_true",
                     help="only time the CPU oracle per configuration beside the GPU (one JSON line each)")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="only run the fixed launch sequence used for per-dispatch counter runs")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -560,6 +601,9 @@ def main():
 
     if args.oracle_table:
         oracle_table()
+        return
+    if args.traffic_probe:
+        traffic_probe()
         return
 
     import torch
