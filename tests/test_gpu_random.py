@@ -16,7 +16,7 @@ from tests.parity import compare
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 40
+N_CASES = 200
 
 
 def _case(i):
