@@ -579,6 +579,8 @@ def main():
                     help="untimed warm-up steps (default: at least 3 and at least 0.3 s of steps, "
                          "so the clocks settle on short workloads too)")
     ap.add_argument("--workload", default="mha24k")
+    ap.add_argument("--dtype", default=None, choices=["bf16", "f32"],
+                    help="run the workload's shape in this input dtype (f32: the exact path)")
     ap.add_argument("--order", default="ring", choices=["ring", "tokenring"])
     ap.add_argument("--unfused", action="store_true", help="separate merge kernel")
     ap.add_argument("--rank", type=int, default=None, help="emulate one rank's share only")
@@ -612,6 +614,8 @@ def main():
     from ring_blockwise_softmax_amd.workloads import WORKLOADS, make_inputs
 
     w = WORKLOADS[args.workload]
+    if args.dtype is not None and args.dtype != w.dtype:
+        w = w.with_(dtype=args.dtype, name=f"{w.name}_{args.dtype}")
     rank = w.rank if args.rank is None else args.rank
     q, k, v = make_inputs(w, device="cuda")
     runner = ra.RingRunner(q, k, v, w.P, layout=w.layout, order=args.order, rank=rank,

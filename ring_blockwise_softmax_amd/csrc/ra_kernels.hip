@@ -602,7 +602,10 @@ __global__ __launch_bounds__(Bf16Cfg<D>::THREADS, Bf16Cfg<D>::OCC) void attn_fwd
 }
 
 // ---------------------------------------------------------------------------
-// fp32 kernel (exact path): v_mfma_f32_32x32x2_f32, no rounding.
+// fp32 kernel (exact path): v_mfma_f32_32x32x2_f32, no rounding.  Bounded
+// for two work-groups per CU (<= 256 registers per lane, two double-buffered
+// padded K/V tiles of 67.6 KB at d = 128), so each SIMD runs two waves and
+// one wave's softmax and tile copy overlap the other's products.
 // ---------------------------------------------------------------------------
 template <int D>
 struct F32Cfg {
@@ -613,10 +616,11 @@ struct F32Cfg {
   static constexpr int CPT = CHUNKS / kThreads;
   static constexpr int TILE_ELEMS = KT * LD;
   static constexpr size_t LDS_BYTES = 2 * 2 * TILE_ELEMS * sizeof(float);
+  static_assert(2 * LDS_BYTES <= 160 * 1024, "LDS of two resident work-groups");
 };
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 1) void attn_fwd_f32(const AttnArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_f32(const AttnArgs a) {
   using C = F32Cfg<D>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   float *smem = reinterpret_cast<float *>(smem_raw);
