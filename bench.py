@@ -107,6 +107,23 @@ def visible_pairs(w, rank=None):
     raise ValueError(w.layout)
 
 
+def select_workload(name, dtype=None):
+    """The named workload, optionally with its inputs in another dtype (same
+    shape, seed and value recipe).  A changed dtype also changes the name, so
+    a traffic record taken on the named workload is not applied to it."""
+    from ring_blockwise_softmax_amd.workloads import WORKLOADS
+
+    w = WORKLOADS[name]
+    if dtype is not None and dtype != w.dtype:
+        w = w.with_(dtype=dtype, name=f"{w.name}_{dtype}")
+    return w
+
+
+def peak_tflops(w):
+    """The dense MFMA peak the attention kernel of workload w is priced against."""
+    return PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
+
+
 def flops_of(w, rank=None):
     return 4.0 * w.head_dim * w.heads_q * w.batch * visible_pairs(w, rank)
 
@@ -613,9 +630,7 @@ def main():
     import ring_blockwise_softmax_amd as ra
     from ring_blockwise_softmax_amd.workloads import WORKLOADS, make_inputs
 
-    w = WORKLOADS[args.workload]
-    if args.dtype is not None and args.dtype != w.dtype:
-        w = w.with_(dtype=args.dtype, name=f"{w.name}_{args.dtype}")
+    w = select_workload(args.workload, args.dtype)
     rank = w.rank if args.rank is None else args.rank
     q, k, v = make_inputs(w, device="cuda")
     runner = ra.RingRunner(q, k, v, w.P, layout=w.layout, order=args.order, rank=rank,
@@ -668,7 +683,7 @@ def main():
     attn_avg_ms = attn_ms / n_attn
     flops_per_launch = total_flops / launches_per_step
     achieved = flops_per_launch / (attn_avg_ms / 1e3) / 1e12
-    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
+    peak = peak_tflops(w)
     if w.layout == "kv_sharded":
         # decode: the attention launch streams K and V once (plus the queries)
         esz = q.element_size()

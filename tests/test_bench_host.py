@@ -70,3 +70,17 @@ def test_clock_summary():
     assert s["socket_power_w"] == 1389
     assert bench.summarize_clock([(["N/A"], "N/A")]) is None
     assert "socket_power_w" not in bench.summarize_clock([([1500], "N/A")])
+
+
+def test_dtype_override_keeps_the_shape_and_prices_fp32_against_its_peak():
+    w = bench.select_workload("mha24k", "f32")
+    base = WORKLOADS["mha24k"]
+    assert (w.dtype, w.name) == ("f32", "mha24k_f32")
+    assert (w.batch, w.heads_q, w.heads_kv, w.head_dim, w.seq_q, w.seq_k, w.P, w.layout, w.seed, w.std) == \
+        (base.batch, base.heads_q, base.heads_kv, base.head_dim, base.seq_q, base.seq_k, base.P, base.layout,
+         base.seed, base.std)
+    assert bench.flops_of(w) == bench.flops_of(base)
+    assert bench.peak_tflops(w) == bench.PEAK_F32_MFMA_TFLOPS and bench.peak_tflops(base) == bench.PEAK_BF16_TFLOPS
+    # the bf16 traffic record never applies to the fp32 run
+    assert bench.measured_traffic(w.name) is None
+    assert bench.select_workload("mha24k", "bf16") is base and bench.select_workload("tiny") is WORKLOADS["tiny"]
