@@ -26,6 +26,9 @@ Prints ONE JSON line.  Extra objects:
                    nominal peak assumes 2.4 GHz).
   merge         -- the standalone merge kernel at the GQA 1M-token share shape
                    (4,194,304 row-heads x d128, 6.49 GB moved), in GB/s.
+  f32_path      -- (headline only) the same shape with fp32 inputs through
+                   the fp32 exact path: ring time and the attention launch
+                   against the 157.3 TFLOP/s fp32 MFMA peak.
   cpu_baseline  -- the fp64 CPU oracle on a bounded sample of the same
                    workload (query rows x all keys), scaled to TFLOP/s; its
                    "check" compares the GPU result on those rows with the
@@ -510,6 +513,52 @@ def mfma_ceiling(grid=2048, iters=2000):
     return out
 
 
+def f32_path_bench(steps=3):
+    """The headline shape on the fp32 exact path (fp32 inputs, fp32 MFMA):
+    the full fused ring, end to end and per attention launch, against the
+    fp32 MFMA peak."""
+    import torch
+
+    import ring_blockwise_softmax_amd as ra
+    from ring_blockwise_softmax_amd.workloads import make_inputs
+
+    w = select_workload("mha24k", "f32")
+    q, k, v = make_inputs(w, device="cuda")
+    runner = ra.RingRunner(q, k, v, w.P, layout=w.layout, fuse_merge=True)
+    for _ in range(2):
+        runner.run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        runner.run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / steps
+    ra.profile_enable(True)
+    for _ in range(steps):
+        runner.run()
+    prof = ra.profile_read()
+    ra.profile_enable(False)
+    n, ms = prof["attn"]
+    flops = flops_of(w)
+    per_launch = flops / (n / steps)
+    achieved = per_launch / (ms / n / 1e3) / 1e12
+    del q, k, v, runner
+    torch.cuda.empty_cache()
+    return {
+        "workload": f"{w.name}: the headline shape with fp32 inputs (kernel attn_fwd_f32<{w.head_dim}>, fused merge)",
+        "steps": steps,
+        "ms_per_step": round(ms_step, 3),
+        "tflops": round(flops / (ms_step / 1e3) / 1e12, 2),
+        "avg_launch_ms": round(ms / n, 3),
+        "achieved": round(achieved, 2),
+        "peak": PEAK_F32_MFMA_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_F32_MFMA_TFLOPS, 4),
+    }
+
+
 def merge_bench(steps=10):
     """Standalone merge at the GQA 1M-token rank-share shape (>= 2 GB)."""
     import torch
@@ -603,6 +652,7 @@ def main():
     ap.add_argument("--rank", type=int, default=None, help="emulate one rank's share only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-merge", action="store_true")
+    ap.add_argument("--no-f32", action="store_true", help="skip the fp32 exact-path run of the headline shape")
     ap.add_argument("--no-clock", action="store_true", help="skip the clock / power sampling")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the MFMA-only ceiling measurement")
     ap.add_argument("--calib-copy", action="store_true",
@@ -764,6 +814,8 @@ def main():
         del src, dst
     if not args.no_merge:
         rec["merge"] = merge_bench()
+    if not args.no_f32 and args.workload == "mha24k" and w.dtype == "bf16":
+        rec["f32_path"] = f32_path_bench()
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, q, k, v, runner.out, runner.lse, rank)
     print(json.dumps(rec), flush=True)
