@@ -39,8 +39,9 @@
  *    the softmax probabilities are rounded to bf16 (round to nearest even)
  *    before the P*V product.  fp32 inputs are computed in fp32 throughout.
  *  - Supported head_dim: 64 and 128.  Sizes up to 2^31-1 tokens per sequence;
- *    head strides (sh) up to 2^31-1 elements; B * Hq * (Sq / 128 + 1024) below
- *    2^31 (one launch counts its work tiles in 32 bits).  Beyond these:
+ *    head strides (sh) up to 2^31-1 elements; bf16 K/V token strides (ss) up
+ *    to (2^31-1-d)/31 elements (about 69 million); B * Hq * (Sq / 128 + 1024)
+ *    below 2^31 (one launch counts its work tiles in 32 bits).  Beyond these:
  *    RA_E_UNSUPPORTED.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Every call is
  *    asynchronous on that stream; device faults surface at the caller's next

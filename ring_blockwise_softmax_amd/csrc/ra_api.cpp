@@ -74,6 +74,13 @@ ra_status check_qkv(const ra_tensor *q, const ra_tensor *k, const ra_tensor *v) 
   if (k->b != q->b || v->b != q->b) return fail(RA_E_INVALID, "batch mismatch");
   if (k->s != v->s || k->h != v->h) return fail(RA_E_INVALID, "k and v shapes differ");
   if (q->h % k->h) return fail(RA_E_INVALID, "Hq (%lld) must be a multiple of Hkv (%lld)", (long long)q->h, (long long)k->h);
+  // The bf16 kernel addresses a K/V tile's rows as 32-bit byte offsets from
+  // the tile's first row: (row * ss + column) * 2 with row < 32 keys.
+  if (q->dtype == RA_BF16) {
+    const int64_t max_ss = (INT32_MAX - q->d) / (kKTileBF16 - 1);
+    if (k->ss > max_ss || v->ss > max_ss)
+      return fail(RA_E_UNSUPPORTED, "k/v token stride beyond %lld elements (bf16)", (long long)max_ss);
+  }
   // Work tiles of one launch are counted in 32 bits: (batch, head, 128-row
   // tile) triples plus a margin for per-item ragged tiles and key splits.
   const double tiles = (double)q->b * (double)q->h * ((double)q->s / 128.0 + 1024.0);

@@ -80,6 +80,7 @@ def test_status_strings():
     (lambda a: a[2].__setattr__("s", 32), RA_E_INVALID),                 # k/v length differ
     (lambda a: a[1].__setattr__("b", 2), RA_E_INVALID),                  # batch mismatch
     (lambda a: a[0].__setattr__("sh", 1 << 33), RA_E_UNSUPPORTED),        # head stride > int32
+    (lambda a: a[2].__setattr__("ss", 72 << 20), RA_E_UNSUPPORTED),       # bf16 V token stride: 32-bit tile offsets
 ])
 def test_block_attn_rejects(mutate, status):
     args = list(good())
@@ -103,6 +104,25 @@ def test_work_tile_count_limit():
     k.h = v.h = 1024
     assert attn(q, k, v, 0, out, lse) == RA_E_UNSUPPORTED
     assert "work-tile" in _L().lib().ra_last_error().decode()
+
+
+def test_bf16_kv_token_stride_limit():
+    """The largest accepted bf16 K/V token stride keeps (31 * ss + d) * 2 bytes
+    within 32 bits; one element more (rounded to a 16-byte multiple) is refused.
+    fp32 K/V address in 64 bits and take the larger stride.  Each call carries
+    an unknown mask kind, which is checked after the tensors, so a stride that
+    passes shows up as the mask error and nothing is ever enqueued."""
+    d = 128
+    lim = (2**31 - 1 - d) // 31
+    ok = lim - lim % 8
+    assert (31 * ok + d) * 2 < 2**32 and 31 * ok + d <= 2**31 - 1
+    for dtype, ss, want in ((0, ok, "mask"), (0, ok + 8, "token stride"), (1, ok + 8, "mask")):
+        q, k, v, out, lse = good(d=d, dtype=dtype)
+        k.ss = ss
+        st = attn(q, k, v, 3, out, lse)
+        msg = _L().lib().ra_last_error().decode()
+        assert want in msg, (dtype, ss, st, msg)
+        assert st == (RA_E_INVALID if want == "mask" else RA_E_UNSUPPORTED)
 
 
 def test_block_attn_rejects_mask():
