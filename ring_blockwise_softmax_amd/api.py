@@ -8,8 +8,9 @@ ring_forward    -- the emulated P-step ring (Ring Attention / TokenRing order,
 ring_plan       -- the host-side work list of the ring
 
 Tensors: q [B, Sq, Hq, d], k/v [B, Sk, Hkv, d] (bf16 or fp32, d contiguous),
-out [B, Sq, Hq, d] fp32, lse [B, Hq, Sq] fp32.  All work is enqueued on the
-current torch stream; nothing synchronises.
+out [B, Sq, Hq, d] fp32, lse [B, Hq, Sq] fp32, all on one GPU.  Work is
+enqueued on ``stream`` (default: torch's current stream); nothing
+synchronises.
 """
 
 from __future__ import annotations
@@ -36,6 +37,16 @@ def _workspace(nbytes, device):
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
+def _on_one_gpu(*tensors):
+    """The kernels dereference every data pointer on the device: refuse host
+    tensors and tensors spread over several GPUs before anything is called."""
+    devs = {t.device for t in tensors if t is not None}
+    if any(d.type != "cuda" for d in devs):
+        raise ValueError("tensors must be on a GPU device (got %s)" % sorted(str(d) for d in devs))
+    if len(devs) > 1:
+        raise ValueError("tensors must be on one GPU (got %s)" % sorted(str(d) for d in devs))
+
+
 def _used_on(stream, *tensors):
     """Mark tensors allocated on torch's current stream as used by ``stream``.
 
@@ -59,6 +70,7 @@ def block_attn_workspace_bytes(q, k) -> int:
 
 def block_attn_fwd(q, k, v, mask="none", out=None, lse=None, workspace=None, stream=None):
     """block_out, block_lse of q against (k, v); mask: none | causal | causal_bottom_right."""
+    _on_one_gpu(q, k, v, out, lse, workspace)
     lib = L.lib()
     if out is None or lse is None:
         out, lse = _empty_out(q)
@@ -78,6 +90,7 @@ def block_attn_fwd_noalloc(q, k, v, out, lse, mask="none", stream=None):
     """block_attn_fwd into caller-provided out/lse with no allocation at all:
     split-K partials use the library's static device scratch (calls that
     overlap in time on one GPU race; calls in one stream are ordered)."""
+    _on_one_gpu(q, k, v, out, lse)
     lib = L.lib()
     tq, tk, tv = L.bshd(q), L.bshd(k), L.bshd(v)
     to, tl = L.bshd(out), L.lse_desc(lse)
@@ -88,6 +101,7 @@ def block_attn_fwd_noalloc(q, k, v, out, lse, mask="none", stream=None):
 
 def merge(out, lse, block_out, block_lse, stream=None):
     """In place: (out, lse) <- sigma-rule merge with (block_out, block_lse)."""
+    _on_one_gpu(out, lse, block_out, block_lse)
     lib = L.lib()
     to, tl = L.bshd(out), L.lse_desc(lse)
     tbo, tbl = L.bshd(block_out), L.lse_desc(block_lse)
@@ -115,6 +129,7 @@ class RingRunner:
 
     def __init__(self, q, k, v, P, layout="contig", order="ring", rank=-1, fuse_merge=True,
                  out=None, lse=None, workspace=None):
+        _on_one_gpu(q, k, v, out, lse, workspace)
         self.lib = L.lib()
         if out is None or lse is None:
             out, lse = _empty_out(q)
@@ -158,7 +173,8 @@ def ring_plan(Sq, Sk, P, layout="contig", order="ring", rank=-1):
     if n < 0:
         raise ValueError(f"no ring plan for Sq={Sq} Sk={Sk} P={P} layout={layout} rank={rank}")
     arr = (L.RaPlanItem * max(n, 1))()
-    lib.ra_ring_plan(Sq, Sk, P, ctypes.byref(lay), arr, n)
+    if lib.ra_ring_plan(Sq, Sk, P, ctypes.byref(lay), arr, n) != n:
+        raise RuntimeError("ring plan changed size between the count and the fill")
     items = []
     for it in arr[:n]:
         items.append({

@@ -249,3 +249,23 @@ def test_noalloc_rejects_before_any_hip_call():
     assert need == 512 * 32 * 4 * 129 * 4 > L.NOALLOC_SCRATCH_BYTES
     assert call(q, k, v, 0, o, l) == RA_E_UNSUPPORTED
     assert b"static scratch" in lib.ra_last_error()
+
+
+@pytest.mark.parametrize("entry", ["block_attn_fwd", "merge", "ring_forward", "noalloc"])
+def test_python_entry_points_refuse_host_tensors(entry):
+    """Host tensors would hand host pointers to the kernels: the binding
+    refuses them before calling the library."""
+    import torch
+    import ring_blockwise_softmax_amd as ra
+    q = torch.zeros(1, 64, 2, 64, dtype=torch.bfloat16)
+    out = torch.zeros(1, 64, 2, 64)
+    lse = torch.zeros(1, 2, 64)
+    with pytest.raises(ValueError, match="GPU"):
+        if entry == "block_attn_fwd":
+            ra.block_attn_fwd(q, q, q)
+        elif entry == "merge":
+            ra.merge(out, lse, out.clone(), lse.clone())
+        elif entry == "ring_forward":
+            ra.ring_forward(q, q, q, 2)
+        else:
+            ra.block_attn_fwd_noalloc(q, q, q, out, lse)
