@@ -29,6 +29,12 @@ Prints ONE JSON line.  Extra objects:
   f32_path      -- (headline only) the same shape with fp32 inputs through
                    the fp32 exact path: ring time and the attention launch
                    against the 157.3 TFLOP/s fp32 MFMA peak.
+  other_workloads -- (headline only) zigzag24k, gqa1m (rank-0 share),
+                   mqa_decode and prefill_chunk, each as --workload NAME runs
+                   it, in compact form: ms per step, TFLOP/s, and the
+                   attention kernel against its roofline.
+Profiling runs of the headline pass --no-f32 --no-others so the kernel
+statistics hold the headline's launches only.
   cpu_baseline  -- the fp64 CPU oracle on a bounded sample of the same
                    workload (query rows x all keys), scaled to TFLOP/s; its
                    "check" compares the GPU result on those rows with the
@@ -637,6 +643,105 @@ def merge_step_bench(steps=12, sets=4):
             "achieved_GBs": nbytes / per / 1e6, "frac": nbytes / per / 1e6 / PEAK_HBM_GBS}
 
 
+def time_runner(runner, steps, warmup=None):
+    """Warm-up (a fixed count, or at least 3 steps and 0.3 s so the clocks
+    settle on short workloads too), then three timed regions of `steps` steps:
+    the steps alone between two events (ms_step), the same steps with the
+    library's event pair around every kernel launch (per-kernel times), and
+    one event pair per step (the spread)."""
+    import torch
+
+    import ring_blockwise_softmax_amd as ra
+
+    if warmup is not None:
+        for _ in range(warmup):
+            runner.run()
+        torch.cuda.synchronize()
+    else:
+        warmup, t0 = 0, time.perf_counter()
+        while warmup < 3 or time.perf_counter() - t0 < 0.3:
+            runner.run()
+            warmup += 1
+            if warmup % 3 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        runner.run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / steps
+    ra.profile_enable(True)
+    for _ in range(steps):
+        runner.run()
+    torch.cuda.synchronize()
+    prof = ra.profile_read()
+    ra.profile_enable(False)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        a.record(stream)
+        runner.run()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return {"warmup": warmup, "steps": steps, "ms_step": ms_step,
+            "per_step": sorted(a.elapsed_time(b) for a, b in evs), "prof": prof}
+
+
+def roofline_of(w, rank, elem_size, tm):
+    """The attention kernel against its roofline: algorithmic flops per launch
+    over the average launch time (MFMA peak of the input dtype), or for the
+    decode layout the K/V (+Q) bytes per launch over it (HBM peak)."""
+    n_attn, attn_ms = tm["prof"]["attn"]
+    launches_per_step = n_attn / tm["steps"]
+    attn_avg_ms = attn_ms / n_attn
+    flops_per_launch = flops_of(w, rank) / launches_per_step
+    if w.layout == "kv_sharded":
+        kv_bytes = 2 * w.batch * w.seq_k * w.heads_kv * w.head_dim * elem_size
+        q_bytes = w.batch * w.seq_q * w.heads_q * w.head_dim * elem_size
+        bytes_per_launch = (kv_bytes + q_bytes) / launches_per_step
+        roof = {"bound": "hbm", "achieved": round(bytes_per_launch / (attn_avg_ms / 1e3) / 1e9, 2),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "algorithmic_bytes_per_launch": bytes_per_launch}
+    else:
+        roof = {"bound": "mfma", "achieved": round(flops_per_launch / (attn_avg_ms / 1e3) / 1e12, 2),
+                "peak": peak_tflops(w), "unit": "TFLOP/s", "flops_per_launch": flops_per_launch}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    return roof, launches_per_step, attn_avg_ms
+
+
+def other_workloads(names=("zigzag24k", "gqa1m", "mqa_decode", "prefill_chunk")):
+    """The other configurations, each as it is run by --workload NAME (default
+    rank, Ring order, fused), in a compact record: end-to-end rate and the
+    attention kernel against its roofline."""
+    import torch
+
+    import ring_blockwise_softmax_amd as ra
+    from ring_blockwise_softmax_amd.workloads import make_inputs
+
+    res = {}
+    for name in names:
+        w = select_workload(name)
+        q, k, v = make_inputs(w, device="cuda")
+        runner = ra.RingRunner(q, k, v, w.P, layout=w.layout, rank=w.rank, fuse_merge=True)
+        steps = 2 if name == "gqa1m" else 10
+        tm = time_runner(runner, steps, 1 if name == "gqa1m" else None)
+        roof, launches, avg_ms = roofline_of(w, w.rank, q.element_size(), tm)
+        res[name] = {
+            "workload": f"B{w.batch} Hq{w.heads_q}/Hkv{w.heads_kv} d{w.head_dim} Sq{w.seq_q} Sk{w.seq_k} "
+                        f"P={w.P} ({w.layout}), {'all ranks' if w.rank < 0 else f'rank {w.rank}'}",
+            "steps": steps, "warmup": tm["warmup"],
+            "ms_per_step": round(tm["ms_step"], 4),
+            "tflops": round(flops_of(w, w.rank) / (tm["ms_step"] / 1e3) / 1e12, 2),
+            "kernel": {"launches_per_step": launches, "avg_launch_ms": round(avg_ms, 4),
+                       **{k_: v_ for k_, v_ in roof.items() if k_ in ("bound", "achieved", "peak", "unit", "frac")}},
+        }
+        del q, k, v, runner
+        torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -653,6 +758,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-merge", action="store_true")
     ap.add_argument("--no-f32", action="store_true", help="skip the fp32 exact-path run of the headline shape")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the compact runs of the other configurations after the headline")
     ap.add_argument("--no-clock", action="store_true", help="skip the clock / power sampling")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the MFMA-only ceiling measurement")
     ap.add_argument("--calib-copy", action="store_true",
@@ -678,74 +785,20 @@ def main():
     import torch
 
     import ring_blockwise_softmax_amd as ra
-    from ring_blockwise_softmax_amd.workloads import WORKLOADS, make_inputs
+    from ring_blockwise_softmax_amd.workloads import make_inputs
 
     w = select_workload(args.workload, args.dtype)
     rank = w.rank if args.rank is None else args.rank
     q, k, v = make_inputs(w, device="cuda")
     runner = ra.RingRunner(q, k, v, w.P, layout=w.layout, order=args.order, rank=rank,
                            fuse_merge=not args.unfused)
-    if args.warmup is not None:
-        for _ in range(args.warmup):
-            runner.run()
-        torch.cuda.synchronize()
-    else:
-        args.warmup, t0 = 0, time.perf_counter()
-        while args.warmup < 3 or time.perf_counter() - t0 < 0.3:
-            runner.run()
-            args.warmup += 1
-            if args.warmup % 3 == 0:
-                torch.cuda.synchronize()
-        torch.cuda.synchronize()
-
-    # Timed region 1: the steps alone (bracketed by synchronisation).
-    stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(args.steps):
-        runner.run()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / args.steps
-    # Timed region 2: the same steps with a HIP event pair around every kernel
-    # launch (recorded by the library on the launch stream) for the per-kernel
-    # roofline; kept apart so the event records do not perturb ms_per_step.
-    ra.profile_enable(True)
-    for _ in range(args.steps):
-        runner.run()
-    torch.cuda.synchronize()
-    prof = ra.profile_read()
-    ra.profile_enable(False)
-    # Timed region 3: one event pair per step, for the spread over steps.
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for a, b in evs:
-        a.record(stream)
-        runner.run()
-        b.record(stream)
-    torch.cuda.synchronize()
-    per_step = sorted(a.elapsed_time(b) for a, b in evs)
-
+    tm = time_runner(runner, args.steps, args.warmup)
+    args.warmup = tm["warmup"]
+    ms_step, per_step = tm["ms_step"], tm["per_step"]
     total_flops = flops_of(w, rank)
     tflops = total_flops / (ms_step / 1e3) / 1e12
-    n_attn, attn_ms = prof["attn"]
-    launches_per_step = n_attn / args.steps
-    attn_avg_ms = attn_ms / n_attn
-    flops_per_launch = total_flops / launches_per_step
-    achieved = flops_per_launch / (attn_avg_ms / 1e3) / 1e12
+    roof, launches_per_step, attn_avg_ms = roofline_of(w, rank, q.element_size(), tm)
     peak = peak_tflops(w)
-    if w.layout == "kv_sharded":
-        # decode: the attention launch streams K and V once (plus the queries)
-        esz = q.element_size()
-        kv_bytes = 2 * w.batch * w.seq_k * w.heads_kv * w.head_dim * esz
-        q_bytes = w.batch * w.seq_q * w.heads_q * w.head_dim * esz
-        bytes_per_launch = (kv_bytes + q_bytes) / launches_per_step
-        roof = {"bound": "hbm", "achieved": round(bytes_per_launch / (attn_avg_ms / 1e3) / 1e9, 2),
-                "peak": PEAK_HBM_GBS, "unit": "GB/s", "algorithmic_bytes_per_launch": bytes_per_launch}
-        roof["frac"] = round(roof["achieved"] / PEAK_HBM_GBS, 4)
-    else:
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "flops_per_launch": flops_per_launch}
 
     rec = {
         "metric": "attention TFLOP/s + % bf16 MFMA peak at S=24000, H=32, d=128, 1 GPU",
@@ -816,6 +869,8 @@ def main():
         rec["merge"] = merge_bench()
     if not args.no_f32 and args.workload == "mha24k" and w.dtype == "bf16":
         rec["f32_path"] = f32_path_bench()
+    if not args.no_others and args.workload == "mha24k" and w.dtype == "bf16":
+        rec["other_workloads"] = other_workloads()
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, q, k, v, runner.out, runner.lse, rank)
     print(json.dumps(rec), flush=True)
