@@ -29,10 +29,11 @@ Prints ONE JSON line.  Extra objects:
   f32_path      -- (headline only) the same shape with fp32 inputs through
                    the fp32 exact path: ring time and the attention launch
                    against the 157.3 TFLOP/s fp32 MFMA peak.
-  other_workloads -- (headline only) zigzag24k, gqa1m (rank-0 share),
-                   mqa_decode and prefill_chunk, each as --workload NAME runs
-                   it, in compact form: ms per step, TFLOP/s, and the
-                   attention kernel against its roofline.
+  other_workloads -- (headline only) the mha24k rank-0 share, zigzag24k
+                   (all ranks and the rank-0 share), gqa1m (rank-0 share),
+                   mqa_decode and prefill_chunk, each as --workload NAME
+                   [--rank R] runs it, in compact form: ms per step, TFLOP/s,
+                   and the attention kernel against its roofline.
 Profiling runs of the headline pass --no-f32 --no-others so the kernel
 statistics hold the headline's launches only.
   cpu_baseline  -- the fp64 CPU oracle on a bounded sample of the same
@@ -711,29 +712,32 @@ def roofline_of(w, rank, elem_size, tm):
     return roof, launches_per_step, attn_avg_ms
 
 
-def other_workloads(names=("zigzag24k", "gqa1m", "mqa_decode", "prefill_chunk")):
+def other_workloads(names=("mha24k@0", "zigzag24k", "zigzag24k@0", "gqa1m", "mqa_decode", "prefill_chunk")):
     """The other configurations, each as it is run by --workload NAME (default
-    rank, Ring order, fused), in a compact record: end-to-end rate and the
-    attention kernel against its roofline."""
+    rank, Ring order, fused; NAME@R: --workload NAME --rank R, one rank's
+    share), in a compact record: end-to-end rate and the attention kernel
+    against its roofline."""
     import torch
 
     import ring_blockwise_softmax_amd as ra
     from ring_blockwise_softmax_amd.workloads import make_inputs
 
     res = {}
-    for name in names:
+    for key in names:
+        name, _, r = key.partition("@")
         w = select_workload(name)
+        rank = int(r) if r else w.rank
         q, k, v = make_inputs(w, device="cuda")
-        runner = ra.RingRunner(q, k, v, w.P, layout=w.layout, rank=w.rank, fuse_merge=True)
+        runner = ra.RingRunner(q, k, v, w.P, layout=w.layout, rank=rank, fuse_merge=True)
         steps = 2 if name == "gqa1m" else 10
         tm = time_runner(runner, steps, 1 if name == "gqa1m" else None)
-        roof, launches, avg_ms = roofline_of(w, w.rank, q.element_size(), tm)
-        res[name] = {
+        roof, launches, avg_ms = roofline_of(w, rank, q.element_size(), tm)
+        res[key] = {
             "workload": f"B{w.batch} Hq{w.heads_q}/Hkv{w.heads_kv} d{w.head_dim} Sq{w.seq_q} Sk{w.seq_k} "
-                        f"P={w.P} ({w.layout}), {'all ranks' if w.rank < 0 else f'rank {w.rank}'}",
+                        f"P={w.P} ({w.layout}), {'all ranks' if rank < 0 else f'rank {rank}'}",
             "steps": steps, "warmup": tm["warmup"],
             "ms_per_step": round(tm["ms_step"], 4),
-            "tflops": round(flops_of(w, w.rank) / (tm["ms_step"] / 1e3) / 1e12, 2),
+            "tflops": round(flops_of(w, rank) / (tm["ms_step"] / 1e3) / 1e12, 2),
             "kernel": {"launches_per_step": launches, "avg_launch_ms": round(avg_ms, 4),
                        **{k_: v_ for k_, v_ in roof.items() if k_ in ("bound", "achieved", "peak", "unit", "frac")}},
         }
