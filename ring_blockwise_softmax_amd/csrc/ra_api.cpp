@@ -495,8 +495,8 @@ ra_status ra_merge(ra_tensor *out, ra_tensor *lse, const ra_tensor *bout, const 
   if (lse->b != out->b || lse->s != out->s || lse->h != out->h || blse->b != out->b || blse->s != out->s ||
       blse->h != out->h)
     return fail(RA_E_INVALID, "lse shapes must be [B, S, H] of out");
+  if (out->b == 0 || out->s == 0) return RA_OK;  // nothing to merge (empty tensors may share a null pointer)
   if (out->data == bout->data) return fail(RA_E_INVALID, "out must not alias block_out");
-  if (out->b == 0 || out->s == 0) return RA_OK;
   MergeArgs m{};
   m.out = (float *)out->data, m.lse = (float *)lse->data;
   m.bout = (const float *)bout->data, m.blse = (const float *)blse->data;

@@ -212,6 +212,34 @@ def test_ring_forward_matches_oracle(name, B, S, Hq, Hkv, d, P, layout, dtype, o
     compare(f"ring {name} {order} fuse={fuse}", out, lse, ro, rl, dtype)
 
 
+@pytest.mark.parametrize("fuse", [True, False])
+@pytest.mark.parametrize("order", ["ring", "tokenring"])
+@pytest.mark.parametrize("layout,S", [("zigzag_causal", 32 * 45), ("contig", 16 * 70), ("contig_causal", 16 * 50)])
+def test_ring_forward_largest_ring(layout, S, order, fuse):
+    """P = 16, the largest ring: the zigzag steps put 2 items per rank, 32 in
+    one launch (the size of a launch's item table), with ragged tiles."""
+    ra = _ra()
+    import torch
+    q, k, v = _inputs(1, S, S, 4, 2, 64, "bf16", seed=S + 16)
+    out, lse = ra.ring_forward(q, k, v, 16, layout=layout, order=order, fuse_merge=fuse)
+    torch.cuda.synchronize()
+    ro, rl = attention(q.cpu(), k.cpu(), v.cpu(), causal=(layout != "contig"))
+    compare(f"ring P=16 {layout} {order} fuse={fuse}", out, lse, ro, rl, "bf16")
+
+
+def test_empty_batch_is_a_noop():
+    """B = 0: every entry point returns with nothing to do."""
+    ra = _ra()
+    import torch
+    q, k, v = _inputs(0, 64, 64, 2, 2, 64, "bf16", seed=5)
+    out, lse = ra.block_attn_fwd(q, k, v)
+    assert out.shape == (0, 64, 2, 64) and lse.shape == (0, 2, 64)
+    out, lse = ra.ring_forward(q, k, v, 4, layout="zigzag_causal")
+    ra.merge(out, lse, out.clone(), lse.clone())
+    torch.cuda.synchronize()
+    assert out.numel() == 0
+
+
 @pytest.mark.parametrize("rank", [0, 3])
 @pytest.mark.parametrize("fuse", [True, False])
 def test_ring_forward_single_rank_share(rank, fuse):
