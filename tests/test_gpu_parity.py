@@ -227,6 +227,21 @@ def test_ring_forward_largest_ring(layout, S, order, fuse):
     compare(f"ring P=16 {layout} {order} fuse={fuse}", out, lse, ro, rl, "bf16")
 
 
+@pytest.mark.parametrize("fuse", [True, False])
+@pytest.mark.parametrize("order", ["ring", "tokenring"])
+def test_kv_sharded_without_keys(order, fuse):
+    """Sk = 0 over P = 4 empty shards: every row sees no key, so it keeps the
+    merge rule's identity (out = 0, lse = -inf), also after the reduction."""
+    ra = _ra()
+    import torch
+    q, k, v = _inputs(2, 3, 0, 8, 2, 128, "bf16", seed=9)
+    out = torch.full((2, 3, 8, 128), 7.0, device="cuda")
+    lse = torch.full((2, 8, 3), 7.0, device="cuda")
+    ra.ring_forward(q, k, v, 4, layout="kv_sharded", order=order, fuse_merge=fuse, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+
+
 def test_empty_batch_is_a_noop():
     """B = 0: every entry point returns with nothing to do."""
     ra = _ra()
