@@ -84,3 +84,26 @@ def test_dtype_override_keeps_the_shape_and_prices_fp32_against_its_peak():
     # the bf16 traffic record never applies to the fp32 run
     assert bench.measured_traffic(w.name) is None
     assert bench.select_workload("mha24k", "bf16") is base and bench.select_workload("tiny") is WORKLOADS["tiny"]
+
+
+def test_roofline_arithmetic():
+    """achieved = algorithmic flops per launch / average launch time, frac =
+    achieved / peak of the input dtype; decode is priced in K/V(+Q) bytes
+    against the HBM peak.  Figures worked by hand from the definitions."""
+    w = WORKLOADS["mha24k"]
+    tm = {"steps": 10, "prof": {"attn": (40, 80.0)}}          # 4 launches per step, 2 ms each
+    roof, launches, avg_ms = bench.roofline_of(w, -1, 2, tm)
+    assert launches == 4 and avg_ms == 2.0
+    assert roof["flops_per_launch"] == 9437184000000.0 / 4
+    assert roof["achieved"] == round(2.359296e12 / 2e-3 / 1e12, 2) == 1179.65
+    assert roof["frac"] == round(1179.65 / 2516.6, 4) and roof["unit"] == "TFLOP/s"
+    f32 = bench.select_workload("mha24k", "f32")
+    roof32, _, _ = bench.roofline_of(f32, -1, 4, tm)
+    assert roof32["peak"] == 157.3 and roof32["frac"] == round(1179.65 / 157.3, 4)
+    d = WORKLOADS["mqa_decode"]                                # B16, 262144 keys, 1 K/V head, d128, bf16
+    tmd = {"steps": 20, "prof": {"attn": (20, 6.4)}}          # one launch per step, 0.32 ms
+    rd, _, _ = bench.roofline_of(d, -1, 2, tmd)
+    kv = 2 * 16 * 262144 * 1 * 128 * 2
+    qb = 16 * 1 * 32 * 128 * 2
+    assert rd["bound"] == "hbm" and rd["algorithmic_bytes_per_launch"] == kv + qb
+    assert rd["achieved"] == round((kv + qb) / 0.32e-3 / 1e9, 2) and rd["peak"] == 8000.0
