@@ -36,6 +36,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "ra.h"
@@ -309,7 +310,12 @@ typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 
 // NT: K/V are streamed once (no other work-group reads them), so their
 // copies carry the non-temporal hint.
-template <int D, bool NT>
+// ROT: for launches of a few rounds of work-groups.  The work-groups that
+// start together on a CU would otherwise finish far apart (the oldest wave
+// issues first) with nothing left to fill the CU; here they take turns at
+// the highest wave priority, one ring period of tiles at a time, from a
+// phase hashed from the work-group index, so they progress evenly.
+template <int D, bool NT, bool ROT = false>
 __global__ __launch_bounds__(Bf16Cfg<D>::THREADS, Bf16Cfg<D>::OCC) void attn_fwd_bf16(const AttnArgs a) {
   using C = Bf16Cfg<D>;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[];
@@ -579,7 +585,14 @@ __global__ __launch_bounds__(Bf16Cfg<D>::THREADS, Bf16Cfg<D>::OCC) void attn_fwd
   const int npro = min(ntiles, C::PF);
   for (int j = 0; j < npro; ++j) issue_next(j);
   int ti = 0;
+  const int rot0 = (int)((blockIdx.x * 2654435761u) >> 30) % 3;
   for (; ti < nt_main; ti += C::NBUF) {
+    if constexpr (ROT) {
+      const int p = (ti / C::NBUF + rot0) % 3;
+      if (p == 0) __builtin_amdgcn_s_setprio(2);
+      else if (p == 1) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
+    }
 #pragma unroll
     for (int k = 0; k < C::NBUF; ++k) {
       if (ti + k >= ntiles) break;
@@ -588,6 +601,7 @@ __global__ __launch_bounds__(Bf16Cfg<D>::THREADS, Bf16Cfg<D>::OCC) void attn_fwd
       step(ti + k, k, ti + k + C::PF < ntiles, (k + C::PF) % C::NBUF);
     }
   }
+  if constexpr (ROT) __builtin_amdgcn_s_setprio(0);
   for (; ti < ntiles; ti += C::NBUF) {  // copies only
 #pragma unroll
     for (int k = 0; k < C::NBUF; ++k) {
@@ -1037,15 +1051,15 @@ __global__ __launch_bounds__(kRowsThreads) void split_reduce_rows_kernel(const S
 // ---------------------------------------------------------------------------
 static __device__ __align__(256) unsigned char scratch[RA_NOALLOC_SCRATCH_BYTES];
 
-constexpr int kMaxScratchDevices = 64;
+constexpr int kMaxDevices = 64;
 
 int noalloc_scratch(void **ptr, size_t *bytes) {
   static std::mutex mu;
-  static void *addr[kMaxScratchDevices] = {};
+  static void *addr[kMaxDevices] = {};
   int dev = 0;
   hipError_t rc = hipGetDevice(&dev);
   if (rc != hipSuccess) return (int)rc;
-  if (dev < 0 || dev >= kMaxScratchDevices) return (int)hipErrorInvalidDevice;
+  if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
   std::lock_guard<std::mutex> lk(mu);
   if (addr[dev] == nullptr) {
     void *p = nullptr;
@@ -1070,12 +1084,33 @@ static int allow_lds(K kernel, size_t bytes) {
   return (int)hipFuncSetAttribute((const void *)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
-template <int D, bool NT>
+template <int D, bool NT, bool ROT>
 static int launch_bf16(const AttnArgs &a, dim3 grid, hipStream_t s) {
-  static const int attr = allow_lds(attn_fwd_bf16<D, NT>, Bf16Cfg<D>::LDS_BYTES);
+  static const int attr = allow_lds(attn_fwd_bf16<D, NT, ROT>, Bf16Cfg<D>::LDS_BYTES);
   if (attr) return attr;
-  attn_fwd_bf16<D, NT><<<grid, dim3(Bf16Cfg<D>::THREADS), Bf16Cfg<D>::LDS_BYTES, s>>>(a);
+  attn_fwd_bf16<D, NT, ROT><<<grid, dim3(Bf16Cfg<D>::THREADS), Bf16Cfg<D>::LDS_BYTES, s>>>(a);
   return 0;
+}
+
+// Compute units of the current device, read once per device.
+static int cu_count() {
+  static std::atomic<int> cache[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// Rotating priorities pay in launches of up to about four rounds of resident
+// work-groups (one rank's ring step, one block); in long launches the usual
+// oldest-first order keeps the copy pipelines steadier.
+template <int D>
+static bool few_rounds(dim3 grid) {
+  return (int64_t)grid.x <= (int64_t)4 * cu_count() * Bf16Cfg<D>::OCC;
 }
 
 template <int D>
@@ -1096,9 +1131,11 @@ int launch_attn(const AttnArgs &a, int dtype, int head_dim, void *stream) {
     bool streamed = a.GP == a.G;
     for (int i = 0; i < a.nitems; ++i) streamed = streamed && a.items[i].nqt == 1;
     if (streamed)
-      rc = head_dim == 128 ? launch_bf16<128, true>(a, grid, s) : launch_bf16<64, true>(a, grid, s);
+      rc = head_dim == 128 ? launch_bf16<128, true, false>(a, grid, s) : launch_bf16<64, true, false>(a, grid, s);
+    else if (head_dim == 128)
+      rc = few_rounds<128>(grid) ? launch_bf16<128, false, true>(a, grid, s) : launch_bf16<128, false, false>(a, grid, s);
     else
-      rc = head_dim == 128 ? launch_bf16<128, false>(a, grid, s) : launch_bf16<64, false>(a, grid, s);
+      rc = few_rounds<64>(grid) ? launch_bf16<64, false, true>(a, grid, s) : launch_bf16<64, false, false>(a, grid, s);
   } else {
     rc = head_dim == 128 ? launch_f32<128>(a, grid, block, s) : launch_f32<64>(a, grid, block, s);
   }

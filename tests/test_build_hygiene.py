@@ -42,7 +42,7 @@ def test_kernels_compile_without_inline_asm_warnings(tmp_path):
         return tuple(int(re.search(r"; %s: (\d+)" % key, meta).group(1))
                      for key in ("NumVgprs", "NumAgprs", "ScratchSize", "Occupancy"))
 
-    vgprs, _, scratch, occ = resources("_ZN2ra13attn_fwd_bf16ILi128ELb0EEEvNS_8AttnArgsE")
+    vgprs, _, scratch, occ = resources("_ZN2ra13attn_fwd_bf16ILi128ELb0ELb0EEEvNS_8AttnArgsE")
     assert scratch == 0 and occ >= 3 and vgprs <= 168, (vgprs, scratch, occ)
     # the fp32 exact path: two waves per SIMD (two work-groups per CU)
     for d in (128, 64):
