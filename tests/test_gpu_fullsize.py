@@ -186,12 +186,16 @@ def test_prefill_chunk_sampled():
         compare(f"prefill_chunk kv{g}", out[:, rows_t][:, :, hs], lse[:, hs][:, :, rows_t], ro, rl, w.dtype)
 
 
-@pytest.mark.parametrize("order,fuse", [("ring", True), ("tokenring", False)])
-def test_mqa_decode_full(order, fuse):
-    """MQA decode: B16, 32/1 heads, one query vs 262144 keys over P=8 (all rows)."""
+@pytest.mark.parametrize("order,fuse,dtype", [("ring", True, "bf16"), ("tokenring", False, "bf16"),
+                                              ("ring", True, "f32"), ("tokenring", False, "f32")])
+def test_mqa_decode_full(order, fuse, dtype):
+    """MQA decode: B16, 32/1 heads, one query vs 262144 keys over P=8 (all rows);
+    also with fp32 inputs (the exact path's split-K over 32768-key blocks)."""
     ra = _ra()
     import torch
     w = WORKLOADS["mqa_decode"]
+    if dtype != w.dtype:
+        w = w.with_(dtype=dtype, name=f"mqa_decode_{dtype}")
     q, k, v = make_inputs(w, device="cuda")
     out, lse = ra.ring_forward(q, k, v, w.P, layout=w.layout, order=order, fuse_merge=fuse)
     torch.cuda.synchronize()
