@@ -159,12 +159,16 @@ def test_gqa_1m_rank_share_sampled(rank, kv_heads):
         compare(f"gqa1m rank{rank} kv{g}", out[:, rows_t][:, :, hs], lse[:, hs][:, :, rows_t], ro, rl, w.dtype)
 
 
-def test_prefill_chunk_sampled():
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefill_chunk_sampled(dtype):
     """Chunked prefill at full size: the last 4096 of 131072 tokens, GQA 32/8,
-    K/V in 8 shards (gather-merge path), sampled rows against the oracle."""
+    K/V in 8 shards (gather-merge path), sampled rows against the oracle; also
+    with fp32 inputs through the exact path."""
     ra = _ra()
     import torch
     w = WORKLOADS["prefill_chunk"]
+    if dtype != w.dtype:
+        w = w.with_(dtype=dtype, name=f"prefill_chunk_{dtype}")
     print("[fullsize] prefill_chunk: generating inputs on the GPU", flush=True)
     q, k, v = make_inputs(w, device="cuda")
     runner = ra.RingRunner(q, k, v, w.P, layout=w.layout, order=w.order, fuse_merge=True)
