@@ -64,11 +64,13 @@ def _cached_inputs(w):
 
 
 @pytest.mark.parametrize("order,fuse", [("ring", True), ("tokenring", True), ("ring", False)])
-@pytest.mark.parametrize("name", ["mha24k", "zigzag24k"])
+@pytest.mark.parametrize("name", ["mha24k", "zigzag24k", "mha24k_f32"])
 def test_24k_configs_sampled(name, order, fuse):
+    """mha24k_f32: the headline shape with fp32 inputs (the benchmark's
+    exact-path run), 32 heads."""
     ra = _ra()
     import torch
-    w = WORKLOADS[name]
+    w = WORKLOADS[name] if name in WORKLOADS else WORKLOADS["mha24k"].with_(name=name, dtype="f32")
     q, k, v = _cached_inputs(w)
     runner = ra.RingRunner(q, k, v, w.P, layout=w.layout, order=order, rank=w.rank, fuse_merge=fuse)
     out, lse = runner.run()
