@@ -85,6 +85,36 @@ def test_24k_configs_sampled(name, order, fuse):
     assert torch.isfinite(out).all() and torch.isfinite(lse).all()
 
 
+@pytest.mark.parametrize("name,order", [("mha24k", "ring"), ("zigzag24k", "tokenring")])
+def test_24k_rank0_share_sampled(name, order):
+    """One rank's share at full size (the shape each GPU runs in a real ring):
+    its launches are one or two rounds of work-groups, which the launcher runs
+    with rotating wave priorities.  Sampled rows of rank 0 against the oracle,
+    and the rows rank 0 does not own stay untouched."""
+    ra = _ra()
+    import torch
+    from oracle.blockwise import contiguous_shares, zigzag_chunks
+    w = WORKLOADS[name]
+    q, k, v = _cached_inputs(w)
+    out = torch.full((w.batch, w.seq_q, w.heads_q, w.head_dim), 5.0, device="cuda")
+    lse = torch.full((w.batch, w.heads_q, w.seq_q), 5.0, device="cuda")
+    ra.ring_forward(q, k, v, w.P, layout=w.layout, order=order, rank=0, out=out, lse=lse)
+    torch.cuda.synchronize()
+    owned = np.asarray((zigzag_chunks(w.seq_q, w.P) if w.layout == "zigzag_causal"
+                        else contiguous_shares(w.seq_q, w.P))[0], dtype=np.int64)
+    rng = np.random.default_rng(w.seed + 100)
+    edges = [owned[0], owned[1], owned[127], owned[128], owned[-1], owned[len(owned) // 2 - 1], owned[len(owned) // 2]]
+    rows = np.array(sorted(set(int(r) for r in edges) | set(rng.choice(owned, 16, replace=False).tolist())),
+                    dtype=np.int64)
+    print(f"[fullsize] {name} rank 0 {order}: oracle on {len(rows)} rows x {w.heads_q} heads", flush=True)
+    ro, rl = attention(q.cpu(), k.cpu(), v.cpu(), causal=(w.layout != "contig"), rows=rows)
+    rows_t = torch.as_tensor(rows, device="cuda")
+    compare(f"{name} rank 0 {order} sampled", out[:, rows_t], lse[:, :, rows_t], ro, rl, w.dtype)
+    not_owned = torch.ones(w.seq_q, dtype=torch.bool, device="cuda")
+    not_owned[torch.as_tensor(owned, device="cuda")] = False
+    assert torch.all(out[:, not_owned] == 5.0) and torch.all(lse[:, :, not_owned] == 5.0)
+
+
 # The medium fp32 configuration: the 24k sequence over a 4-rank ring with 4
 # heads, fp32 N(0,1) inputs (the tiny configuration's distribution), so every
 # block is a 6000-key loop ending in a 16-key ragged tile (6000 = 187*32 + 16)
