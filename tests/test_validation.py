@@ -269,3 +269,41 @@ def test_python_entry_points_refuse_host_tensors(entry):
             ra.ring_forward(q, q, q, 2)
         else:
             ra.block_attn_fwd_noalloc(q, q, q, out, lse)
+
+
+def test_last_error_is_thread_local():
+    """Each host thread reads back the message of its own last failure, even
+    when several threads fail differently at the same time."""
+    import threading
+    lib = _L().lib()
+    barrier = threading.Barrier(4)
+    seen = {}
+
+    def worker(i):
+        q, k, v, out, lse = good()
+        if i == 0:
+            q.dtype = 7                      # unknown dtype
+            want = "unknown dtype"
+        elif i == 1:
+            k.h = v.h = 3                    # Hq % Hkv
+            want = "multiple of Hkv"
+        elif i == 2:
+            out.s = 63                       # out shape
+            want = "out shape"
+        else:
+            want = "unknown mask kind"
+        barrier.wait()
+        msgs = []
+        for _ in range(200):
+            st = attn(q, k, v, 3 if i == 3 else 0, out, lse)
+            assert st != RA_OK
+            msgs.append(lib.ra_last_error().decode())
+        seen[i] = (want, msgs)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(4)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    for i, (want, msgs) in seen.items():
+        assert all(want in m for m in msgs), (i, want, [m for m in msgs if want not in m][:3])
