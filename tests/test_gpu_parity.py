@@ -416,3 +416,39 @@ def test_side_stream_call_keeps_its_workspace():
     torch.cuda.synchronize()
     del junk
     assert torch.equal(o, ref_o) and torch.equal(l, ref_l)
+
+
+def test_concurrent_host_threads_on_two_streams():
+    """Two host threads call the library at the same time on two streams of
+    default priority (first-use kernel set-up, the device-attribute cache and
+    the launch path run concurrently); each result is bitwise equal to the same
+    call made alone on the current stream."""
+    import threading
+    import torch
+    ra = _ra()
+    cases = [(2400, "zigzag_causal", "bf16", 11), (1000, "contig", "f32", 12)]
+    inputs = [_inputs(1, S, S, 4, 2, 128, dt, seed=sd) for S, _, dt, sd in cases]
+    ref = [ra.ring_forward(q, k, v, 4, layout=lay) for (q, k, v), (_, lay, _, _) in zip(inputs, cases)]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    got = [None, None]
+    barrier = threading.Barrier(2)
+
+    def worker(i):
+        q, k, v = inputs[i]
+        barrier.wait()
+        with torch.cuda.stream(streams[i]):
+            res = []
+            for _ in range(5):
+                res.append(ra.ring_forward(q, k, v, 4, layout=cases[i][1], stream=streams[i]))
+            got[i] = res
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    for i in range(2):
+        for out, lse in got[i]:
+            assert torch.equal(out, ref[i][0]) and torch.equal(lse, ref[i][1]), f"case {i}"
